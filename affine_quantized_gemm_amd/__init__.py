@@ -1,0 +1,164 @@
+"""Python binding of libqmm (affine group-quantized small-M matmul, MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libqmm.so``; PyTorch supplies device memory and the current stream.  The
+C entry points are exposed under their C names (``qmm_quantize``,
+``qmm_dequantize``, ``qmm_small_m``, ...) taking integer addresses, and
+tensor-level helpers (:func:`quantize`, :func:`dequantize`, :func:`small_m`)
+mirror the MLX-style API the pages use: ``quantize(w, group_size, bits) ->
+(wq, scales, biases)`` and ``quantized_matmul(x, wq, scales, biases,
+transpose=True, ...)`` (MLX issue #4720, "To Reproduce").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqmm.so")
+
+QMM_F16, QMM_BF16 = 0, 1
+QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_MISALIGNED, QMM_ERR_HIP = 0, -1, -2, -3, -4
+KERNEL_VALU, KERNEL_MFMA_REG, KERNEL_MFMA_LDS = 0, 1, 2
+KERNEL_IDS = (KERNEL_VALU, KERNEL_MFMA_REG, KERNEL_MFMA_LDS)
+
+_DT = {torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
+
+EXPORTS = (
+    "qmm_quantize", "qmm_dequantize", "qmm_small_m", "qmm_small_m_forced",
+    "qmm_select_kernel", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
+)
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        from . import build as _b
+        _b.build(verbose=False)
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    sig = {
+        "qmm_quantize": (i32, [i32, i32, i32, i64, i64, vp, vp, vp, vp, vp]),
+        "qmm_dequantize": (i32, [i32, i32, i32, i64, i64, vp, vp, vp, vp, vp]),
+        "qmm_small_m": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "qmm_small_m_forced": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32]),
+        "qmm_select_kernel": (i32, [i32, i32, i32, i64, i64, i64]),
+        "qmm_packed_words": (i64, [i32, i64]),
+        "qmm_strerror": (ctypes.c_char_p, [i32]),
+        "qmm_kernel_name": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+# ---- C entry points under their C names (integer addresses, status codes) ----
+qmm_quantize = _lib.qmm_quantize
+qmm_dequantize = _lib.qmm_dequantize
+qmm_small_m = _lib.qmm_small_m
+qmm_small_m_forced = _lib.qmm_small_m_forced
+qmm_select_kernel = _lib.qmm_select_kernel
+qmm_packed_words = _lib.qmm_packed_words
+
+
+def strerror(status: int) -> str:
+    return _lib.qmm_strerror(int(status)).decode()
+
+
+def kernel_name(kernel_id: int) -> str:
+    return _lib.qmm_kernel_name(int(kernel_id)).decode()
+
+
+def packed_words(bits: int, K: int) -> int:
+    return int(_lib.qmm_packed_words(int(bits), int(K)))
+
+
+def select_kernel(dtype, bits: int, group_size: int, M: int, N: int, K: int) -> int:
+    return int(_lib.qmm_select_kernel(_dt(dtype), bits, group_size, M, N, K))
+
+
+# ---- tensor helpers ----
+
+def _dt(dtype) -> int:
+    if dtype not in _DT:
+        raise QmmError(QMM_ERR_UNSUPPORTED, f"dtype {dtype}")
+    return _DT[dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, what: str):
+    if status != QMM_OK:
+        raise QmmError(status, what)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize(w: torch.Tensor, bits: int, group_size: int, stream=None):
+    """W [N, K] (fp16/bf16, GPU) -> (wq [N, K*bits/32] int32 words, scales, biases)."""
+    _dev(w, "w")
+    N, K = w.shape
+    nw = packed_words(bits, K)
+    if nw < 0 or K % group_size:
+        raise QmmError(QMM_ERR_UNSUPPORTED, "quantize shape")
+    wq = torch.empty((N, nw), dtype=torch.int32, device=w.device)
+    sc = torch.empty((N, K // group_size), dtype=w.dtype, device=w.device)
+    bi = torch.empty_like(sc)
+    _check(qmm_quantize(_dt(w.dtype), bits, group_size, N, K, w.data_ptr(), wq.data_ptr(),
+                        sc.data_ptr(), bi.data_ptr(), _stream(stream)), "qmm_quantize")
+    return wq, sc, bi
+
+
+def dequantize(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int, group_size: int,
+               stream=None) -> torch.Tensor:
+    """(wq, scales, biases) -> W_hat [N, K] in the scales' dtype."""
+    for t, n in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    N = wq.shape[0]
+    K = scales.shape[1] * group_size
+    out = torch.empty((N, K), dtype=scales.dtype, device=wq.device)
+    _check(qmm_dequantize(_dt(scales.dtype), bits, group_size, N, K, wq.data_ptr(), scales.data_ptr(),
+                          biases.data_ptr(), out.data_ptr(), _stream(stream)), "qmm_dequantize")
+    return out
+
+
+def small_m(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+            group_size: int, out: torch.Tensor | None = None, kernel: int | None = None,
+            stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] . dequant(wq, scales, biases)^T (``kernel`` forces a variant)."""
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    M, K = x.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+            biases.data_ptr(), out.data_ptr(), _stream(stream))
+    if kernel is None:
+        _check(qmm_small_m(*args), "qmm_small_m")
+    else:
+        _check(qmm_small_m_forced(*args, int(kernel)), "qmm_small_m_forced")
+    return out

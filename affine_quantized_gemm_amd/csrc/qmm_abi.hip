@@ -1,0 +1,134 @@
+// extern "C" boundary of libqmm: argument validation, kernel selection and
+// launches on the caller's stream.  Declarations and contracts: qmm.h.
+//
+// Unsupported formats are an explicit error here.  The pages' own wrapper
+// silently falls back to a stock kernel when given unsupported parameters
+// ("What Are NAX Verify Kernels and When Is the Turbo Profile Activated in
+// MTPLX?", "Frequently Asked Questions"); this library has one code path per
+// variant and reports QMM_ERR_UNSUPPORTED instead.
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "qmm.h"
+#include "qmm_internal.hpp"
+#include "qmm_dispatch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_format(int dt, int bits, int gs, int64_t N, int64_t K) {
+    if (N < 0 || K < 0) return QMM_ERR_INVALID_ARG;
+    if (dt != QMM_F16 && dt != QMM_BF16) return QMM_ERR_UNSUPPORTED;
+    if (bits != 4 && bits != 6 && bits != 8) return QMM_ERR_UNSUPPORTED;
+    if (gs != 32 && gs != 64 && gs != 128) return QMM_ERR_UNSUPPORTED;
+    if (K < 64 || K % 64 != 0 || K % gs != 0) return QMM_ERR_UNSUPPORTED;
+    // grid-size limits of the launchers (N*K/32 threads in a 32-bit grid)
+    if (N > INT32_MAX || K > INT32_MAX) return QMM_ERR_UNSUPPORTED;
+    if ((N * (K / 32) + 255) / 256 > INT32_MAX) return QMM_ERR_UNSUPPORTED;
+    return QMM_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (p == nullptr) return QMM_ERR_INVALID_ARG;
+    for (const void* p : ps)
+        if (!aligned16(p)) return QMM_ERR_MISALIGNED;
+    return QMM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+int check_matmul(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, const void* x, const uint32_t* wq,
+                 const void* scales, const void* biases, void* y) {
+    if (M < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, gs, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    return check_ptrs({x, wq, scales, biases, y});
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_quantize(int dt, int bits, int group_size, int64_t N, int64_t K, const void* w, uint32_t* wq, void* scales,
+                 void* biases, void* stream) {
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (N == 0) return QMM_OK;
+    st = check_ptrs({w, wq, scales, biases});
+    if (st != QMM_OK) return st;
+    return hip_status(qmm::launch_quantize(dt, bits, group_size, w, wq, scales, biases, N, K,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int qmm_dequantize(int dt, int bits, int group_size, int64_t N, int64_t K, const uint32_t* wq, const void* scales,
+                   const void* biases, void* w_out, void* stream) {
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (N == 0) return QMM_OK;
+    st = check_ptrs({wq, scales, biases, w_out});
+    if (st != QMM_OK) return st;
+    return hip_status(qmm::launch_dequantize(dt, bits, group_size, wq, scales, biases, w_out, N, K,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int qmm_select_kernel(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K) {
+    if (M < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    return qmm::select_kernel(dt, bits, group_size, M, N, K);
+}
+
+int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                       const uint32_t* wq, const void* scales, const void* biases, void* y, void* stream,
+                       int kernel_id) {
+    int st = check_matmul(dt, bits, group_size, M, N, K, x, wq, scales, biases, y);
+    if (st != QMM_OK) return st;
+    if (!qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K)) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream)};
+    return hip_status(qmm::launch_kernel(kernel_id, a));
+}
+
+int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                const uint32_t* wq, const void* scales, const void* biases, void* y, void* stream) {
+    int st = check_matmul(dt, bits, group_size, M, N, K, x, wq, scales, biases, y);
+    if (st != QMM_OK) return st;
+    if (M == 0 || N == 0) return QMM_OK;
+    const int kid = qmm::select_kernel(dt, bits, group_size, M, N, K);
+    qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream)};
+    return hip_status(qmm::launch_kernel(kid, a));
+}
+
+int64_t qmm_packed_words(int bits, int64_t K) {
+    if (bits != 4 && bits != 6 && bits != 8) return -1;
+    if (K < 0 || (K * bits) % 32 != 0) return -1;
+    return K * bits / 32;
+}
+
+const char* qmm_strerror(int status) {
+    switch (status) {
+        case QMM_OK: return "ok";
+        case QMM_ERR_INVALID_ARG: return "invalid argument (negative size or null pointer)";
+        case QMM_ERR_UNSUPPORTED: return "unsupported format or shape";
+        case QMM_ERR_MISALIGNED: return "array base pointer not 16-byte aligned";
+        case QMM_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* qmm_kernel_name(int kernel_id) {
+    switch (kernel_id) {
+        case QMM_KERNEL_VALU: return "valu_splitfree";
+        case QMM_KERNEL_MFMA_REG: return "mfma_splitfree_reg";
+        case QMM_KERNEL_MFMA_LDS: return "mfma_lds";
+        default: return "?";
+    }
+}
+
+}  // extern "C"

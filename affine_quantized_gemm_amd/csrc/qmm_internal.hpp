@@ -1,0 +1,28 @@
+// Launchers shared between the libqmm translation units (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+hipError_t launch_quantize(int dt, int bits, int gs, const void* w, uint32_t* wq, void* s, void* b,
+                           int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_dequantize(int dt, int bits, int gs, const uint32_t* wq, const void* s, const void* b,
+                             void* out, int64_t N, int64_t K, hipStream_t st);
+
+// Arguments of one small-M matmul call (validated by the ABI layer).
+struct MatmulArgs {
+    int dt, bits, gs;
+    int64_t M, N, K;
+    const void* x;
+    const uint32_t* wq;
+    const void* scales;
+    const void* biases;
+    void* y;
+    hipStream_t stream;
+};
+
+hipError_t launch_valu(const MatmulArgs& a);
+
+}  // namespace qmm

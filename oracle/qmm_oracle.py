@@ -31,6 +31,8 @@ are silent the choices are:
 * q is fitted against the *stored* scale, with round-half-to-even;
 * a constant group (max == min) stores scale 0 and q = 0, which dequantizes
   exactly to the bias;
+* a group whose minimum is a zero stores the bias +0 (signed zeros compare
+  equal, so the minimum's sign would otherwise depend on element order);
 * packing is a little-endian bitstream per row: value k occupies bits
   [bits*k, bits*k + bits), stored as little-endian uint32 words (4-bit:
   8 values per word, low nibble first; 8-bit: 4 per word; 6-bit: 4 values
@@ -181,7 +183,9 @@ def quantize(w: np.ndarray, dt: str, bits: int, group_size: int):
     Q = np.float32((1 << bits) - 1)
     wf = to_f32(w, dt).reshape(N, G, group_size)
     assert np.all(np.isfinite(wf)), "inputs must be finite"
-    lo = wf.min(axis=-1)
+    # A zero minimum is taken as +0 so that the bias does not depend on the
+    # order in which -0 and +0 are met (adding +0 maps -0 to +0 exactly).
+    lo = (wf.min(axis=-1) + np.float32(0.0)).astype(np.float32)
     hi = wf.max(axis=-1)
     span = (hi - lo).astype(np.float32)                      # fl32(hi - lo)
     assert np.all(np.isfinite(span)), "group range must be finite in fp32"
@@ -190,7 +194,7 @@ def quantize(w: np.ndarray, dt: str, bits: int, group_size: int):
     s = to_f32(s_dt, dt)
     b_dt = f32_to_dt_rne(lo, dt)                            # exact: lo is a dtype value
     b = to_f32(b_dt, dt)
-    assert np.array_equal(b, lo)
+    assert np.array_equal(b, lo) and not np.any(np.signbit(b) & (b == 0))
     diff = (wf - b[..., None]).astype(np.float32)            # fl32(w - b)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = (diff / s[..., None]).astype(np.float32)         # fl32(diff / s)

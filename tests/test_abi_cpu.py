@@ -1,0 +1,116 @@
+"""The C-ABI library loads without a GPU, exports every symbol qmm.h
+declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import affine_quantized_gemm_amd as Q
+
+A = 0x10000          # a 16-byte-aligned fake address (never dereferenced)
+MIS = 0x10008        # misaligned fake address
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qmm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"qmm_quantize", "qmm_dequantize", "qmm_small_m"} <= set(names)
+    lib = ctypes.CDLL(Q.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Q.EXPORTS)
+
+
+def mm(dt=0, bits=4, gs=64, M=4, N=64, K=256, x=A, wq=A, s=A, b=A, y=A):
+    return Q.qmm_small_m(dt, bits, gs, M, N, K, x, wq, s, b, y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), Q.QMM_ERR_UNSUPPORTED),
+    (dict(bits=2), Q.QMM_ERR_UNSUPPORTED),
+    (dict(gs=48), Q.QMM_ERR_UNSUPPORTED),
+    (dict(gs=16), Q.QMM_ERR_UNSUPPORTED),
+    (dict(gs=128, K=192), Q.QMM_ERR_UNSUPPORTED),
+    (dict(K=96, gs=32), Q.QMM_ERR_UNSUPPORTED),
+    (dict(K=32, gs=32), Q.QMM_ERR_UNSUPPORTED),
+    (dict(K=0), Q.QMM_ERR_UNSUPPORTED),
+    (dict(M=65), Q.QMM_ERR_UNSUPPORTED),
+    (dict(dt=2), Q.QMM_ERR_UNSUPPORTED),
+    (dict(dt=-1), Q.QMM_ERR_UNSUPPORTED),
+    (dict(M=-1), Q.QMM_ERR_INVALID_ARG),
+    (dict(N=-3), Q.QMM_ERR_INVALID_ARG),
+    (dict(K=-64), Q.QMM_ERR_INVALID_ARG),
+    (dict(x=None), Q.QMM_ERR_INVALID_ARG),
+    (dict(wq=None), Q.QMM_ERR_INVALID_ARG),
+    (dict(s=None), Q.QMM_ERR_INVALID_ARG),
+    (dict(b=None), Q.QMM_ERR_INVALID_ARG),
+    (dict(y=None), Q.QMM_ERR_INVALID_ARG),
+    (dict(x=MIS), Q.QMM_ERR_MISALIGNED),
+    (dict(wq=MIS), Q.QMM_ERR_MISALIGNED),
+    (dict(y=MIS), Q.QMM_ERR_MISALIGNED),
+    (dict(M=0, x=None, y=None), Q.QMM_OK),     # empty problem: nothing launched
+    (dict(N=0, wq=None, s=None, b=None, y=None), Q.QMM_OK),
+])
+def test_small_m_validation(kw, status):
+    assert mm(**kw) == status
+
+
+def test_forced_validation():
+    args = (0, 4, 64, 4, 64, 256, A, A, A, A, A, None)
+    assert Q.qmm_small_m_forced(*args, 99) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_forced(*args, -1) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_forced(0, 5, 64, 4, 64, 256, A, A, A, A, A, None, 0) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_forced(0, 4, 64, 0, 64, 256, None, A, A, A, None, None, 0) == Q.QMM_OK
+
+
+def test_quantize_dequantize_validation():
+    qz = Q.qmm_quantize
+    assert qz(0, 7, 64, 8, 256, A, A, A, A, None) == Q.QMM_ERR_UNSUPPORTED
+    assert qz(0, 4, 64, 8, 100, A, A, A, A, None) == Q.QMM_ERR_UNSUPPORTED
+    assert qz(0, 4, 64, -8, 256, A, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
+    assert qz(0, 4, 64, 8, 256, None, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
+    assert qz(0, 4, 64, 8, 256, A, MIS, A, A, None) == Q.QMM_ERR_MISALIGNED
+    assert qz(1, 6, 32, 0, 256, None, None, None, None, None) == Q.QMM_OK
+    dq = Q.qmm_dequantize
+    assert dq(3, 4, 64, 8, 256, A, A, A, A, None) == Q.QMM_ERR_UNSUPPORTED
+    assert dq(0, 4, 64, 8, 256, A, A, None, A, None) == Q.QMM_ERR_INVALID_ARG
+    assert dq(0, 4, 64, 8, 256, A, A, A, MIS, None) == Q.QMM_ERR_MISALIGNED
+    assert dq(0, 8, 128, 0, 256, None, None, None, None, None) == Q.QMM_OK
+
+
+def test_helpers():
+    assert Q.packed_words(4, 4096) == 512
+    assert Q.packed_words(6, 4096) == 768
+    assert Q.packed_words(8, 64) == 16
+    assert Q.packed_words(5, 64) == -1
+    assert Q.packed_words(6, 48) == 9
+    assert Q.packed_words(6, 4) == -1
+    assert Q.strerror(Q.QMM_ERR_MISALIGNED).startswith("array base pointer")
+    assert Q.strerror(12345) == "unknown status"
+    names = {Q.kernel_name(k) for k in Q.KERNEL_IDS}
+    assert len(names) == len(Q.KERNEL_IDS) and "?" not in names
+    assert Q.kernel_name(17) == "?"
+
+
+def test_select_kernel_is_total_over_supported_shapes():
+    import torch
+    for dt in (torch.float16, torch.bfloat16):
+        for bits in (4, 6, 8):
+            for gs in (32, 64, 128):
+                for M in (1, 2, 4, 6, 8, 9, 16, 17, 32, 36, 48, 64):
+                    for N, K in ((1, 64 * 2), (1024, 4096), (4096, 14336), (151936, 4096)):
+                        if K % gs:
+                            continue
+                        k = Q.select_kernel(dt, bits, gs, M, N, K)
+                        assert k in Q.KERNEL_IDS, (dt, bits, gs, M, N, K, k)
+    assert Q.select_kernel(torch.float16, 4, 64, 65, 64, 256) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.select_kernel(torch.float16, 4, 64, -1, 64, 256) == Q.QMM_ERR_INVALID_ARG

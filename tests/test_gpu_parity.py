@@ -1,0 +1,192 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+quantize / dequantize must match bit for bit; the matmul must satisfy
+|y - y_oracle| <= 4e-3 * sum_k |x_k| |w_hat_k| + 1e-3 elementwise.
+Every call goes through the C ABI (via the thin binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import qmm_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+COMBOS = [(dt, bits, gs) for dt in ("f16", "bf16") for bits in (4, 6, 8) for gs in (32, 64, 128)]
+
+
+@pytest.fixture(scope="module")
+def Q():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import affine_quantized_gemm_amd as Q
+    return Q
+
+
+def weight_sets(dt, N, K, gs, seed):
+    return {
+        "normal": synth.normal((N, K), 0.02, dt, seed),
+        "outlier": synth.normal((N, K), 0.02, dt, seed + 1, outlier_frac=0.01),
+        "mixed": synth.special_groups("mixed", N, K, gs, dt, seed + 2),
+        "tiny": synth.special_groups("tiny", N, K, gs, dt, seed + 3),
+        "constant": synth.special_groups("constant", N, K, gs, dt, seed + 4),
+    }
+
+
+def oracle_quant(w_cpu, dt, bits, gs):
+    return O.quantize(synth.to_oracle(w_cpu), dt, bits, gs)
+
+
+@pytest.mark.parametrize("dt,bits,gs", COMBOS)
+def test_quantize_dequantize_bit_exact(Q, dt, bits, gs):
+    N, K = 40, 512
+    for kind, w in weight_sets(dt, N, K, gs, 100 + bits + gs).items():
+        print(f"quantize {dt} bits={bits} gs={gs} kind={kind}", flush=True)
+        wq, sc, bi = Q.quantize(w.cuda(), bits, gs)
+        torch.cuda.synchronize()
+        owq, osc, obi = oracle_quant(w, dt, bits, gs)
+        assert np.array_equal(synth.to_oracle(wq), owq), kind
+        assert np.array_equal(synth.to_oracle(sc).view(np.uint16), osc.view(np.uint16)), kind
+        assert np.array_equal(synth.to_oracle(bi).view(np.uint16), obi.view(np.uint16)), kind
+        # dequantize from the oracle's own packed weights
+        d = Q.dequantize(synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(),
+                         synth.from_oracle(obi, dt).cuda(), bits, gs)
+        torch.cuda.synchronize()
+        od = O.dequantize(owq, osc, obi, dt, bits, gs, K)
+        assert np.array_equal(synth.to_oracle(d).view(np.uint16), od.view(np.uint16)), kind
+
+
+def run_case(Q, dt, bits, gs, M, N, K, seed, kernel=None, outlier=0.0, wstd=0.02):
+    w = synth.normal((N, K), wstd, dt, seed, outlier_frac=outlier)
+    x = synth.normal((M, K), 1.0, dt, seed + 1)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    y = Q.small_m(x.cuda(), synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(),
+                  synth.from_oracle(obi, dt).cuda(), bits, gs, kernel=kernel)
+    torch.cuda.synchronize()
+    yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+    yg = O.to_f64(synth.to_oracle(y), dt)
+    return O.within_tolerance(yg, yo, T)
+
+
+def supported(Q, kernel, M):
+    return kernel in (None, Q.KERNEL_VALU, Q.KERNEL_MFMA_LDS) or M <= 16
+
+
+KERNELS = [None, 0, 1, 2]
+
+
+@pytest.mark.parametrize("dt,bits,gs", COMBOS)
+@pytest.mark.parametrize("M", [1, 4, 6, 8])
+def test_small_m_formats(Q, dt, bits, gs, M):
+    N, K = 80, 512
+    for kernel in KERNELS:
+        if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+            continue
+        print(f"small_m {dt} b{bits} gs{gs} M={M} kernel={kernel}", flush=True)
+        ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=7 * M + bits, kernel=kernel)
+        assert ok, (kernel, worst)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [2, 3, 5, 7, 12, 16, 24, 32, 36, 48, 64])
+def test_small_m_all_m(Q, dt, M):
+    N, K = 144, 1024
+    for kernel in KERNELS:
+        if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+            continue
+        print(f"small_m {dt} M={M} kernel={kernel}", flush=True)
+        ok, worst = run_case(Q, dt, 4, 64, M, N, K, seed=300 + M, kernel=kernel, outlier=0.01)
+        assert ok, (kernel, worst)
+
+
+def kernel_built(Q, kernel):
+    """A variant is built if the forced entry point accepts an empty problem."""
+    return Q.qmm_small_m_forced(0, 4, 64, 0, 16, 256, None, None, None, None, None, None, kernel) == Q.QMM_OK
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(1, 1, 64, 64), (3, 17, 128, 32), (8, 1000, 128, 128), (64, 33, 192, 64),
+                                      (16, 15, 64, 32), (6, 4099, 256, 128)])
+def test_edge_shapes(Q, M, N, K, gs):
+    for dt in ("f16", "bf16"):
+        for bits in (4, 6, 8):
+            for kernel in KERNELS:
+                if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+                    continue
+                print(f"edge {dt} b{bits} M={M} N={N} K={K} gs={gs} kernel={kernel}", flush=True)
+                ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=M + N + K, kernel=kernel)
+                assert ok, (dt, bits, kernel, worst)
+
+
+def test_empty_problems(Q):
+    x = torch.zeros((0, 256), dtype=torch.float16, device="cuda")
+    w = synth.normal((16, 256), 0.02, "f16", 1).cuda()
+    wq, sc, bi = Q.quantize(w, 4, 64)
+    y = Q.small_m(x, wq, sc, bi, 4, 64)
+    assert y.shape == (0, 16)
+    w0 = torch.zeros((0, 256), dtype=torch.float16, device="cuda")
+    wq0, sc0, bi0 = Q.quantize(w0, 4, 64)
+    y0 = Q.small_m(torch.ones((4, 256), dtype=torch.float16, device="cuda"), wq0, sc0, bi0, 4, 64)
+    assert y0.shape == (4, 0)
+
+
+def test_one_hot_rows_equal_dequantized_weights_valu(Q):
+    """With one-hot x the group-factored VALU kernel forms fl32(s*q + b) and
+    rounds it once, which is exactly the dequantize output."""
+    for dt, bits, gs in (("f16", 4, 64), ("bf16", 8, 32), ("f16", 6, 128)):
+        K, N = 256, 48
+        w = synth.normal((N, K), 0.02, dt, 5).cuda()
+        wq, sc, bi = Q.quantize(w, bits, gs)
+        d = Q.dequantize(wq, sc, bi, bits, gs)
+        for k0 in range(0, K, 8):
+            x = torch.zeros((8, K), dtype=DT[dt], device="cuda")
+            x[torch.arange(8), torch.arange(k0, k0 + 8)] = 1
+            y = Q.small_m(x, wq, sc, bi, bits, gs, kernel=Q.KERNEL_VALU)
+            assert torch.equal(y.view(torch.int16), d[:, k0:k0 + 8].t().contiguous().view(torch.int16))
+
+
+def test_padded_zero_rows_are_inert(Q):
+    """Zero rows appended to x give zero outputs and leave the other rows
+    bit-for-bit unchanged (rows are independent in every variant)."""
+    for kernel in KERNELS[1:]:
+        if not kernel_built(Q, kernel):
+            continue
+        K, N = 512, 64
+        w = synth.normal((N, K), 0.02, "f16", 9).cuda()
+        wq, sc, bi = Q.quantize(w, 4, 64)
+        x = synth.normal((5, K), 1.0, "f16", 10).cuda()
+        xp = torch.cat([x, torch.zeros((3, K), dtype=x.dtype, device="cuda")])
+        y = Q.small_m(x, wq, sc, bi, 4, 64, kernel=kernel)
+        yp = Q.small_m(xp, wq, sc, bi, 4, 64, kernel=kernel)
+        assert torch.all(yp[5:] == 0)
+        assert torch.equal(yp[:5].view(torch.int16), y.view(torch.int16)), kernel
+
+
+def test_deterministic(Q):
+    for kernel in KERNELS:
+        if kernel is not None and not kernel_built(Q, kernel):
+            continue
+        K, N, M = 4096, 4096, 6
+        w = synth.normal((N, K), 0.02, "f16", 11).cuda()
+        wq, sc, bi = Q.quantize(w, 4, 64)
+        x = synth.normal((M, K), 1.0, "f16", 12).cuda()
+        y0 = Q.small_m(x, wq, sc, bi, 4, 64, kernel=kernel)
+        for _ in range(20):
+            y = Q.small_m(x, wq, sc, bi, 4, 64, kernel=kernel)
+            assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+
+
+def test_errors_raise(Q):
+    w = synth.normal((16, 256), 0.02, "f16", 1).cuda()
+    wq, sc, bi = Q.quantize(w, 4, 64)
+    x = torch.ones((4, 264), dtype=torch.float16, device="cuda")[:, 8:]
+    with pytest.raises(ValueError):
+        Q.small_m(x, wq, sc, bi, 4, 64)            # non-contiguous view
+    xm = torch.ones((4 * 256 + 4,), dtype=torch.float16, device="cuda")[4:].view(4, 256)
+    with pytest.raises(Q.QmmError) as e:
+        Q.small_m(xm, wq, sc, bi, 4, 64)            # 8-byte offset: misaligned
+    assert e.value.status == Q.QMM_ERR_MISALIGNED
+    with pytest.raises(Q.QmmError) as e:
+        Q.small_m(torch.ones((65, 256), dtype=torch.float16, device="cuda"), wq, sc, bi, 4, 64)
+    assert e.value.status == Q.QMM_ERR_UNSUPPORTED

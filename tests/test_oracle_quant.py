@@ -189,3 +189,11 @@ def test_q_of_max_is_not_always_Q(golden):
     """With round-up scales q(max) can fall one short of Q (example D)."""
     rows = {r[0]: r for r in golden("quant_worked_examples.txt")}
     assert rows["D"][7].split()[0] == "000000FE"
+
+
+def test_signed_zero_minimum_gives_positive_zero_bias():
+    """A group whose minimum is zero stores bias +0 whatever the order of -0/+0."""
+    for first in (-0.0, 0.0):
+        w = np.array([[first, -first] + [0.5] * 30], dtype=np.float16)
+        _, _, bi = O.quantize(w, "f16", 4, 32)
+        assert bi.view(np.uint16)[0, 0] == 0x0000
