@@ -29,7 +29,7 @@ _DT = {torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
 
 EXPORTS = (
     "qmm_quantize", "qmm_dequantize", "qmm_small_m", "qmm_small_m_forced",
-    "qmm_select_kernel", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
+    "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
 )
 
 
@@ -51,6 +51,7 @@ def _load():
         "qmm_small_m": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "qmm_small_m_forced": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32]),
         "qmm_select_kernel": (i32, [i32, i32, i32, i64, i64, i64]),
+        "qmm_kernel_supported": (i32, [i32, i32, i32, i64, i64, i64, i32]),
         "qmm_packed_words": (i64, [i32, i64]),
         "qmm_strerror": (ctypes.c_char_p, [i32]),
         "qmm_kernel_name": (ctypes.c_char_p, [i32]),
@@ -71,6 +72,7 @@ qmm_small_m = _lib.qmm_small_m
 qmm_small_m_forced = _lib.qmm_small_m_forced
 qmm_select_kernel = _lib.qmm_select_kernel
 qmm_packed_words = _lib.qmm_packed_words
+qmm_kernel_supported = _lib.qmm_kernel_supported
 
 
 def strerror(status: int) -> str:
@@ -87,6 +89,10 @@ def packed_words(bits: int, K: int) -> int:
 
 def select_kernel(dtype, bits: int, group_size: int, M: int, N: int, K: int) -> int:
     return int(_lib.qmm_select_kernel(_dt(dtype), bits, group_size, M, N, K))
+
+
+def kernel_supported(dtype, bits: int, group_size: int, M: int, N: int, K: int, kernel: int) -> bool:
+    return int(_lib.qmm_kernel_supported(_dt(dtype), bits, group_size, M, N, K, int(kernel))) == 1
 
 
 # ---- tensor helpers ----

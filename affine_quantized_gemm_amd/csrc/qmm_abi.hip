@@ -84,6 +84,14 @@ int qmm_select_kernel(int dt, int bits, int group_size, int64_t M, int64_t N, in
     return qmm::select_kernel(dt, bits, group_size, M, N, K);
 }
 
+int qmm_kernel_supported(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int kernel_id) {
+    if (M < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    return qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K) ? 1 : 0;
+}
+
 int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
                        const uint32_t* wq, const void* scales, const void* biases, void* y, void* stream,
                        int kernel_id) {

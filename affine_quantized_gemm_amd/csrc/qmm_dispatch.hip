@@ -4,20 +4,23 @@
 
 namespace qmm {
 
-bool kernel_supports(int kid, int /*dt*/, int /*bits*/, int /*gs*/, int64_t M, int64_t /*N*/, int64_t /*K*/) {
+bool kernel_supports(int kid, int /*dt*/, int bits, int /*gs*/, int64_t M, int64_t /*N*/, int64_t K) {
     switch (kid) {
         case QMM_KERNEL_VALU: return M <= 64;
+        case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, M, K);
         default: return false;
     }
 }
 
-int select_kernel(int /*dt*/, int /*bits*/, int /*gs*/, int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) {
+int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
+    if (kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K)) return QMM_KERNEL_MFMA_REG;
     return QMM_KERNEL_VALU;
 }
 
 hipError_t launch_kernel(int kid, const MatmulArgs& a) {
     switch (kid) {
         case QMM_KERNEL_VALU: return launch_valu(a);
+        case QMM_KERNEL_MFMA_REG: return launch_mfma_reg(a);
         default: return hipErrorInvalidValue;
     }
 }

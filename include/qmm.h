@@ -122,6 +122,11 @@ int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, i
  * negative status if the problem is not supported.  Pure host logic. */
 int qmm_select_kernel(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K);
 
+/* 1 if variant `kernel_id` can run this problem, 0 if it cannot, or a
+ * negative status if the problem itself is invalid or unsupported.  Pure
+ * host logic. */
+int qmm_kernel_supported(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int kernel_id);
+
 /* uint32 words per packed row: K*bits/32 (-1 for unsupported bits or a K
  * that does not fill whole words). */
 int64_t qmm_packed_words(int bits, int64_t K);

@@ -101,6 +101,21 @@ def test_helpers():
     assert Q.kernel_name(17) == "?"
 
 
+def test_kernel_supported():
+    import torch
+    f16 = torch.float16
+    assert Q.kernel_supported(f16, 4, 64, 64, 4096, 4096, Q.KERNEL_VALU)
+    assert not Q.kernel_supported(f16, 4, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 4, 64, 4, 4096, 4096, 42)
+    assert Q.qmm_kernel_supported(0, 5, 64, 4, 64, 256, 0) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_kernel_supported(0, 4, 64, -1, 64, 256, 0) == Q.QMM_ERR_INVALID_ARG
+    # whatever select_kernel picks must itself be supported
+    for M in (1, 4, 6, 8, 16, 17, 32, 64):
+        for K in (512, 4096, 14336):
+            k = Q.select_kernel(f16, 4, 64, M, 4096, K)
+            assert Q.kernel_supported(f16, 4, 64, M, 4096, K, k)
+
+
 def test_select_kernel_is_total_over_supported_shapes():
     import torch
     for dt in (torch.float16, torch.bfloat16):

@@ -70,8 +70,8 @@ def run_case(Q, dt, bits, gs, M, N, K, seed, kernel=None, outlier=0.0, wstd=0.02
     return O.within_tolerance(yg, yo, T)
 
 
-def supported(Q, kernel, M):
-    return kernel in (None, Q.KERNEL_VALU, Q.KERNEL_MFMA_LDS) or M <= 16
+def supported(Q, kernel, M, bits=4, gs=64, N=64, K=512, dt=torch.float16):
+    return kernel is None or Q.kernel_supported(dt, bits, gs, M, N, K, kernel)
 
 
 KERNELS = [None, 0, 1, 2]
@@ -82,7 +82,7 @@ KERNELS = [None, 0, 1, 2]
 def test_small_m_formats(Q, dt, bits, gs, M):
     N, K = 80, 512
     for kernel in KERNELS:
-        if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+        if not supported(Q, kernel, M, bits, gs, N, K, DT[dt]):
             continue
         print(f"small_m {dt} b{bits} gs{gs} M={M} kernel={kernel}", flush=True)
         ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=7 * M + bits, kernel=kernel)
@@ -94,16 +94,15 @@ def test_small_m_formats(Q, dt, bits, gs, M):
 def test_small_m_all_m(Q, dt, M):
     N, K = 144, 1024
     for kernel in KERNELS:
-        if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+        if not supported(Q, kernel, M, 4, 64, N, K, DT[dt]):
             continue
         print(f"small_m {dt} M={M} kernel={kernel}", flush=True)
         ok, worst = run_case(Q, dt, 4, 64, M, N, K, seed=300 + M, kernel=kernel, outlier=0.01)
         assert ok, (kernel, worst)
 
 
-def kernel_built(Q, kernel):
-    """A variant is built if the forced entry point accepts an empty problem."""
-    return Q.qmm_small_m_forced(0, 4, 64, 0, 16, 256, None, None, None, None, None, None, kernel) == Q.QMM_OK
+def kernel_built(Q, kernel, M=6, K=512):
+    return Q.kernel_supported(torch.float16, 4, 64, M, 64, K, kernel)
 
 
 @pytest.mark.parametrize("M,N,K,gs", [(1, 1, 64, 64), (3, 17, 128, 32), (8, 1000, 128, 128), (64, 33, 192, 64),
@@ -112,7 +111,7 @@ def test_edge_shapes(Q, M, N, K, gs):
     for dt in ("f16", "bf16"):
         for bits in (4, 6, 8):
             for kernel in KERNELS:
-                if kernel is not None and (not kernel_built(Q, kernel) or not supported(Q, kernel, M)):
+                if not supported(Q, kernel, M, bits, gs, N, K, DT[dt]):
                     continue
                 print(f"edge {dt} b{bits} M={M} N={N} K={K} gs={gs} kernel={kernel}", flush=True)
                 ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=M + N + K, kernel=kernel)
@@ -168,6 +167,8 @@ def test_deterministic(Q):
         if kernel is not None and not kernel_built(Q, kernel):
             continue
         K, N, M = 4096, 4096, 6
+        if kernel is not None and not kernel_built(Q, kernel, M, K):
+            continue
         w = synth.normal((N, K), 0.02, "f16", 11).cuda()
         wq, sc, bi = Q.quantize(w, 4, 64)
         x = synth.normal((M, K), 1.0, "f16", 12).cuda()
