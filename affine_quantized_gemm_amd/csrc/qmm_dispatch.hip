@@ -4,10 +4,10 @@
 
 namespace qmm {
 
-bool kernel_supports(int kid, int /*dt*/, int bits, int /*gs*/, int64_t M, int64_t /*N*/, int64_t K) {
+bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /*N*/, int64_t K) {
     switch (kid) {
         case QMM_KERNEL_VALU: return M <= 64;
-        case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, M, K);
+        case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, gs, M, K);
         default: return false;
     }
 }

@@ -10,20 +10,28 @@
 //   * the multiply-accumulates run on the matrix cores
 //     (v_mfma_f32_16x16x32_{f16,bf16}); at 4 bits the vector ALUs alone
 //     cannot keep up with the HBM stream for M >= 6;
-//   * the workgroup's 4..8 wavefronts split K among themselves so that each
-//     SIMD streams a distinct part of the tile, and their partial sums are
-//     combined once through LDS at the end of the tile;
-//   * the activation rows stay in registers for the whole kernel while the
-//     workgroup walks over column tiles (persistent grid), so x is read once
-//     per workgroup, not once per tile.
+//   * the workgroup's wavefronts (up to 16) split K among themselves so that
+//     each SIMD streams a distinct part of the tile, and their partial sums
+//     are combined once per tile through LDS;
+//   * each wavefront holds the activation fragments of its part of K in
+//     registers for the whole kernel while the workgroup walks over column
+//     tiles (persistent grid), so x is read once per workgroup, not once per
+//     tile, and the inner loop touches no shared memory.
 //
 // Arithmetic (exact up to fp32 rounding).  Codes become fp16/bf16 values
-// q + OFF with the "magic number" trick (OFF = 1024 for fp16, 128 for bf16
-// at 4/6 bits; 8-bit bf16 converts exactly with OFF = 0).  Per column n and
-// group g the matrix cores produce P = sum x*(q + OFF) and X = sum x, and
-//   y += s*P + (b - OFF*s)*X        (fp32 FMAs, one pair per group portion)
-// which equals sum_k x_k * (s*q_k + b) without rounding the dequantized
-// weight to the activation dtype.
+// q + off with the "magic number" trick: off = 1024 (fp16; 64 for the odd
+// codes of a 4-bit word, which are unpacked without a shift), 128 (bf16 at
+// 4/6 bits) or 0 (8-bit bf16, converted exactly).  For column n, the sum
+// splits into
+//   y = sum_u s_u * P_u  +  sum_u b_u * X_u  -  sum_u s_u * O_u
+// over "units" u (runs of K inside one quantization group), with
+//   P_u = sum_{k in u} x_k * (q_k + off_k)   (matrix cores, per tile),
+//   X_u = sum_{k in u} x_k,  O_u = sum_{k in u} x_k * off_k  (from x only).
+// The first term is one fp32 FMA per output per unit; the other two are
+// small products over units (X and O against the bias and scale vectors of
+// the tile), done on the matrix cores with X and O split into a high and a
+// low fp16/bf16 part so that they keep fp32-level accuracy.  The dequantized
+// weight s*q + b is never rounded to the activation dtype.
 //
 // Operand layout of v_mfma_f32_16x16x32 (verified on the hardware): lane l
 // supplies A[l%16][8*(l/16)+e] and B[8*(l/16)+e][l%16] for e = 0..7 and
@@ -39,6 +47,7 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Frag {  // 8 packed 16-bit values = one MFMA operand of one lane
     uint32_t v[4];
@@ -55,6 +64,8 @@ __device__ __forceinline__ float4_t mfma(const Frag& a, const Frag& b, float4_t 
     }
 }
 
+// Exchange of 32-lane halves / odd and even 16-lane rows between two
+// registers (gfx950 permlane swaps; semantics checked on the hardware).
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
     const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
     a = r[0];
@@ -69,17 +80,26 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 // Per-format constants.  A lane loads one "segment" of SEG codes of its
 // column per k-block; the four k-slot quarters (jj) of a column load four
 // consecutive segments, so a k-block holds KBLK = 4*SEG codes and feeds
-// STEPS = SEG/8 MFMA steps.
+// STEPS = SEG/8 MFMA steps.  A k-block splits into PORTIONS runs of PC
+// codes, each inside one quantization group; a portion is the "unit" of the
+// scale step.
 template <int DT, int BITS, int GS>
 struct Fmt {
     static constexpr int SEG = BITS == 4 ? 32 : 16;      // codes per lane load
     static constexpr int SEG_WORDS = SEG * BITS / 32;    // 4, 3 or 4 words (16, 12, 16 bytes)
     static constexpr int STEPS = SEG / 8;                // MFMA steps per k-block
     static constexpr int KBLK = 4 * SEG;                 // codes per k-block
-    static constexpr int PORTIONS = (KBLK / GS) > 1 ? (KBLK / GS) : 1;  // group portions per k-block
+    static constexpr int PORTIONS = (KBLK / GS) > 1 ? (KBLK / GS) : 1;
     static constexpr int STEPS_PER_PORTION = STEPS / PORTIONS;
-    static constexpr float OFF = (DT == DT_F16) ? 1024.0f : (BITS == 8 ? 0.0f : 128.0f);
-    static constexpr uint32_t ONES = (DT == DT_F16) ? 0x3C003C00u : 0x3F803F80u;
+    static constexpr int PC = KBLK / PORTIONS;           // codes per portion
+    // offset carried by the code at natural position t of an 8-code run
+    __host__ __device__ static constexpr float off(int t) {
+        if (DT == DT_F16 && BITS == 4) return (t & 1) ? 64.0f : 1024.0f;
+        if (DT == DT_F16) return 1024.0f;
+        if (BITS == 8) return 0.0f;
+        return 128.0f;
+    }
+    static constexpr bool HAS_OFF = !(DT == DT_BF16 && BITS == 8);
     // Step s, quarter jj reads its 8 codes from segment SRC_LANE of the
     // k-block, sub-block SRC_SLOT (after the lane swaps that make every step
     // lie inside one quantization group).
@@ -127,31 +147,44 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 
 // Constants of the unpack, kept in VGPRs for and_or().
 struct UnpackConsts {
-    uint32_t nib;    // 0x000F000F
-    uint32_t six;    // 0x0000003F
-    uint32_t six_hi; // 0x003F0000
-    uint32_t magic;  // q + OFF pattern: 0x6400 (fp16) / 0x4300 (bf16) in both halves
+    uint32_t nib;     // 0x000F000F
+    uint32_t nib_hi;  // 0x00F000F0
+    uint32_t six;     // 0x0000003F
+    uint32_t six_hi;  // 0x003F0000
+    uint32_t magic;   // q + off pattern: 0x6400 (fp16, 1024) / 0x4300 (bf16, 128) in both halves
+    uint32_t magic4;  // fp16 with the code in mantissa bits 4..7: 0x5400 = 64, step 1/16
 };
 
 template <int DT>
 __device__ __forceinline__ UnpackConsts unpack_consts() {
     UnpackConsts k;
     k.nib = 0x000F000Fu;
+    k.nib_hi = 0x00F000F0u;
     k.six = 0x3Fu;
     k.six_hi = 0x3F0000u;
     k.magic = (DT == DT_F16) ? 0x64006400u : 0x43004300u;
+    k.magic4 = 0x54005400u;
     // keep them in registers (not folded back into literals)
-    asm volatile("" : "+v"(k.nib), "+v"(k.six), "+v"(k.six_hi), "+v"(k.magic));
+    asm volatile("" : "+v"(k.nib), "+v"(k.nib_hi), "+v"(k.six), "+v"(k.six_hi), "+v"(k.magic), "+v"(k.magic4));
     return k;
 }
 
-// 4-bit: one word (8 codes) -> q + OFF in order 0,4,1,5,2,6,3,7.
+// 4-bit: one word (8 codes) -> q + off in order 0,4,1,5,2,6,3,7.  fp16 takes
+// the odd nibbles in place (64 + q, via magic4), bf16 shifts them down
+// (its 7 mantissa bits cannot hold a code at bits 4..7).
+template <int DT>
 __device__ __forceinline__ Frag unpack4(uint32_t w, const UnpackConsts& k) {
     Frag f;
+    const uint32_t w8 = w >> 8;
     f.v[0] = and_or(w, k.nib, k.magic);
-    f.v[1] = and_or(w >> 4, k.nib, k.magic);
-    f.v[2] = and_or(w >> 8, k.nib, k.magic);
-    f.v[3] = and_or(w >> 12, k.nib, k.magic);
+    f.v[2] = and_or(w8, k.nib, k.magic);
+    if constexpr (DT == DT_F16) {
+        f.v[1] = and_or(w, k.nib_hi, k.magic4);
+        f.v[3] = and_or(w8, k.nib_hi, k.magic4);
+    } else {
+        f.v[1] = and_or(w >> 4, k.nib, k.magic);
+        f.v[3] = and_or(w >> 12, k.nib, k.magic);
+    }
     return f;
 }
 
@@ -203,7 +236,7 @@ __device__ __forceinline__ void segment_frags(uint32_t (&w)[NW], Frag (&b)[NS], 
             swap16(w[2], w[3]);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = unpack4(w[s], k);
+        for (int s = 0; s < 4; ++s) b[s] = unpack4<DT>(w[s], k);
     } else if constexpr (BITS == 8) {
         if constexpr (GS == 32) {
             swap32(w[0], w[2]);
@@ -227,12 +260,11 @@ __device__ __forceinline__ void segment_frags(uint32_t (&w)[NW], Frag (&b)[NS], 
     }
 }
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 template <int BITS, int NW>
 __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ p, uint32_t (&w)[NW]) {
     if constexpr (NW == 4) {
-        // streamed once: non-temporal hint keeps the weights from displacing x
+        // streamed once: the non-temporal hint keeps the weights from
+        // displacing reused data in the caches
         const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
         w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
     } else {
@@ -240,27 +272,6 @@ __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ p, uin
         w[0] = a.x; w[1] = a.y; w[2] = a.z;
     }
 }
-
-// Scale/bias words of one tile for one lane.  Vector form (VEC): the
-// wavefront's NG consecutive groups as NG/2 words (two 16-bit values per
-// word) of scales and of biases.  Scalar form: one value per group portion.
-template <bool VEC, int NGW, int KPW, int NP>
-struct ScaleRegs;
-template <int NGW, int KPW, int NP>
-struct ScaleRegs<true, NGW, KPW, NP> {
-    uint32_t s[NGW], b[NGW];
-};
-template <int NGW, int KPW, int NP>
-struct ScaleRegs<false, NGW, KPW, NP> {
-    uint32_t s[KPW][NP], b[KPW][NP];
-};
-
-// Weight words and raw scale/bias values of one tile for one lane.
-template <bool VEC, int NGW, int KPW, int NW, int NP>
-struct TileRegs {
-    uint32_t w[KPW][NW];
-    ScaleRegs<VEC, NGW, KPW, NP> sb;
-};
 
 template <int NWORDS>
 __device__ __forceinline__ void load_words(const uint16_t* __restrict__ p, uint32_t (&d)[NWORDS]) {
@@ -279,124 +290,229 @@ __device__ __forceinline__ void load_words(const uint16_t* __restrict__ p, uint3
     }
 }
 
-// LDS layout of the staged activations: rows 0..M-1 of x and one zero row
-// (read by the lanes of rows >= M), each row holding the KC = W*KPW*KBLK
-// positions the wavefronts cover (zero beyond K) with every run of 8 values
-// already in the order the weight unpack produces.  Row stride KC + 8 values:
-// the 16-byte pad rotates rows across LDS banks.  Then two buffers of
-// per-wavefront partial sums (one per tile parity).
-__host__ __device__ constexpr int64_t x_stride(int64_t KC) { return KC + 8; }
-__host__ __device__ inline int64_t lds_x_bytes(int64_t M, int64_t KC) { return (M + 1) * x_stride(KC) * 2; }
+// Scale/bias words of one tile for one lane.  Vector form (VEC): the
+// wavefront's NG consecutive groups as NG/2 words (two 16-bit values per
+// word) of scales and of biases.  Scalar form: one value per portion.
+template <bool VEC, int NGW, int KPW, int NP>
+struct ScaleRegs;
+template <int NGW, int KPW, int NP>
+struct ScaleRegs<true, NGW, KPW, NP> {
+    uint32_t s[NGW], b[NGW];
+};
+template <int NGW, int KPW, int NP>
+struct ScaleRegs<false, NGW, KPW, NP> {
+    uint32_t s[KPW][NP], b[KPW][NP];
+};
+
+// Weight words and raw scale/bias values of one tile for one lane.
+template <bool VEC, int NGW, int KPW, int NW, int NP>
+struct TileRegs {
+    uint32_t w[KPW][NW];
+    ScaleRegs<VEC, NGW, KPW, NP> sb;
+};
+
+// Offset carried by the value in slot e of an activation fragment (the
+// fragment holds its 8 codes in the order the weight unpack produces).
+template <int DT, int BITS, int GS>
+__host__ __device__ constexpr float slot_off(int e) {
+    using F = Fmt<DT, BITS, GS>;
+    if constexpr (BITS == 4) {
+        constexpr int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        return F::off(perm[e]);
+    } else if constexpr (BITS == 6) {
+        constexpr int perm[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        return F::off(perm[e]);
+    } else {
+        return F::off(e);
+    }
+}
+
 __host__ __device__ inline int64_t lds_red_bytes(int W) { return 2LL * W * 64 * 4 * 4; }
 
 // W wavefronts per workgroup; wavefront w owns the KPW consecutive k-blocks
 // [w*KPW, (w+1)*KPW) of K.  One workgroup owns a tile of 16 columns at a
 // time and walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...; the loads of
-// the next LA tiles are in flight while a tile is computed (LA+1 register
-// buffers used in turn).  x is staged once per workgroup in LDS; each MFMA
-// step reads its 8-value A fragment with one 16-byte LDS read at a fixed
-// offset from a per-lane base.
+// the next tile are in flight while a tile is computed (two register buffers
+// used in turn).
 //
 // The tile loop is written so that no wait on a load can be forced early:
 // loaded registers are not touched in the iteration that issues them (the
 // memory counter retires in order, so an early use would also wait for every
 // later load), prefetches are unconditional (the last ones re-read the final
-// tile), and nothing on the weight side is masked: positions beyond K read
-// valid addresses and meet zero activations.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, int LA>
-__global__ __launch_bounds__(64 * W, (KPW <= 4 ? 4 : 2)) void mfma_reg_kernel(
+// tile) and pinned ahead of the compute, and nothing on the weight side is
+// masked: positions beyond K read valid addresses and meet zero activations.
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
+__global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
     using F = Fmt<DT, BITS, GS>;
+    constexpr int LA = 1;
     constexpr int NG = (KPW * F::KBLK + GS - 1) / GS;  // groups touched by one wavefront (vector form)
     constexpr int NGW = NG >= 2 ? NG / 2 : 1;            // 32-bit words holding NG 16-bit values
-    constexpr int64_t KC = static_cast<int64_t>(W) * KPW * F::KBLK;
+    constexpr int NU = KPW * F::PORTIONS;                // units (portions) per wavefront
+    static_assert(NU <= 8, "the unit products use the first k-slot quarter only");
     using Regs = TileRegs<VEC, NGW, KPW, F::SEG_WORDS, F::PORTIONS>;
     extern __shared__ __align__(16) uint8_t lds[];
-    uint16_t* xs_lds = reinterpret_cast<uint16_t*>(lds);
-    float* red = reinterpret_cast<float*>(lds + lds_x_bytes(M, KC));
+    float* red = reinterpret_cast<float*>(lds);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int c = lane & 15;   // tile column of this lane's B operand / D output
+    const int c = lane & 15;   // tile column of this lane's B operand / D output, row of its A operand
     const int jj = lane >> 4;  // k-slot quarter
     const int64_t row_words = K * BITS / 32;
     const int64_t G = K / GS;
     const int64_t ntiles = (N + 15) / 16;
     const int64_t kb0 = static_cast<int64_t>(wave) * KPW;
-    constexpr int64_t xstride = x_stride(KC);
+
+    // Tile addressing: a uniform base (scalar registers) plus a per-lane
+    // offset fixed for the whole kernel.  The last tile of a ragged N is
+    // shifted back to end at column N, so no lane ever reads past the last
+    // row; the columns it shares with the previous tile are recomputed and
+    // stored again with bit-identical values.  (N < 16: lanes clamp instead.)
+    const int64_t row_bytes = row_words * 4;
+    const bool narrow = N < 16;
+    const uint32_t lane_row = narrow ? static_cast<uint32_t>(min(static_cast<int64_t>(c), N - 1)) : c;
+    const uint32_t w_off = lane_row * static_cast<uint32_t>(row_bytes) +
+                           static_cast<uint32_t>((kb0 * F::KBLK + jj * F::SEG) * BITS / 8);
+    const uint32_t s_off = lane_row * static_cast<uint32_t>(G) + static_cast<uint32_t>(kb0 * F::KBLK / GS);
+    auto tile_col0 = [&](int64_t tile) -> int64_t {
+        const int64_t c0 = tile * 16;
+        return (narrow || c0 + 16 <= N) ? c0 : N - 16;
+    };
 
     auto load_tile = [&](int64_t tile, Regs& r) {
-        const int64_t n = min(tile * 16 + c, N - 1);  // tail columns re-read the last row
-        const uint32_t* wrow = wq + n * row_words;
+        const int64_t col0 = tile_col0(tile);
+        const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
-            int64_t code0 = (kb0 + i) * F::KBLK + jj * F::SEG;
-            if constexpr (!VEC) code0 = code0 < K ? code0 : K - F::SEG;  // VEC: the k-blocks cover K exactly
-            load_segment<BITS, F::SEG_WORDS>(wrow + code0 * BITS / 32, r.w[i]);
+            if constexpr (VEC) {
+                // VEC: the k-blocks cover K exactly
+                load_segment<BITS, F::SEG_WORDS>(
+                    reinterpret_cast<const uint32_t*>(wbase + w_off + i * (F::KBLK * BITS / 8)), r.w[i]);
+            } else {
+                int64_t code0 = (kb0 + i) * F::KBLK + jj * F::SEG;
+                code0 = code0 < K ? code0 : K - F::SEG;
+                load_segment<BITS, F::SEG_WORDS>(
+                    reinterpret_cast<const uint32_t*>(wbase + lane_row * row_bytes + code0 * BITS / 8), r.w[i]);
+            }
         }
         if constexpr (VEC) {
-            const int64_t g0 = kb0 * F::KBLK / GS;
-            load_words<NGW>(scales + n * G + g0, r.sb.s);
-            load_words<NGW>(biases + n * G + g0, r.sb.b);
+            const uint16_t* sbase = scales + col0 * G;
+            const uint16_t* bbase = biases + col0 * G;
+            load_words<NGW>(sbase + s_off, r.sb.s);
+            load_words<NGW>(bbase + s_off, r.sb.b);
         } else {
 #pragma unroll
             for (int i = 0; i < KPW; ++i)
 #pragma unroll
                 for (int p = 0; p < F::PORTIONS; ++p) {
-                    int64_t g = ((kb0 + i) * F::KBLK + static_cast<int64_t>(p) * (F::KBLK / F::PORTIONS)) / GS;
+                    int64_t g = ((kb0 + i) * F::KBLK + static_cast<int64_t>(p) * F::PC) / GS;
                     g = g < G ? g : G - 1;
-                    r.sb.s[i][p] = scales[n * G + g];
-                    r.sb.b[i][p] = biases[n * G + g];
+                    r.sb.s[i][p] = scales[(col0 + lane_row) * G + g];
+                    r.sb.b[i][p] = biases[(col0 + lane_row) * G + g];
                 }
         }
     };
 
-    // ---- prologue: first tiles' loads in flight, then x staged in LDS
+    // ---- prologue: this wavefront's activation fragments first (rows >= M
+    // and positions >= K read nothing and stay zero), then the first tile
+    uint4 xraw[KPW][F::STEPS];
+    {
+        const bool row_ok = c < M;
+        const uint16_t* xrow = x + static_cast<int64_t>(row_ok ? c : 0) * K;
+#pragma unroll
+        for (int i = 0; i < KPW; ++i)
+#pragma unroll
+            for (int s = 0; s < F::STEPS; ++s) {
+                const int64_t k0 = (kb0 + i) * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
+                xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
+                if (row_ok && (VEC || k0 < K)) xraw[i][s] = *reinterpret_cast<const uint4*>(xrow + k0);
+            }
+    }
     Regs buf[LA + 1];
     const int64_t step = gridDim.x;
     int64_t tile = blockIdx.x;
+    load_tile(min(tile, ntiles - 1), buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    Frag xa[KPW][F::STEPS];
 #pragma unroll
-    for (int a = 0; a < LA; ++a) load_tile(min(tile + a * step, ntiles - 1), buf[a]);
+    for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int s = 0; s < F::STEPS; ++s) xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
+
+    // Unit sums X_u = sum x and O_u = sum x*off of row c over each unit of
+    // this wavefront: per-lane partial sums, then a sum over the four k-slot
+    // quarters (lanes c, c+16, c+32, c+48).  A operands of the unit products
+    // (split hi + lo): lane (row c, quarter 0) holds units 0..NU-1, the other
+    // quarters zero.
+    Frag xhi, xlo, ohi, olo;
     {
-        constexpr int64_t runs = KC / 8;  // 16-byte runs per staged row
-        const int64_t units = static_cast<int64_t>(M + 1) * runs;
-        for (int64_t u = threadIdx.x; u < units; u += 64 * W) {
-            const int64_t m = u / runs;
-            const int64_t k8 = u - m * runs;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M && k8 * 8 < K) v = *reinterpret_cast<const uint4*>(x + m * K + k8 * 8);
-            const Frag f = x_frag<BITS, DT>(v);
-            *reinterpret_cast<uint4*>(xs_lds + m * xstride + k8 * 8) = make_uint4(f.v[0], f.v[1], f.v[2], f.v[3]);
+        float ux[NU], uo[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int i = u / F::PORTIONS, p = u % F::PORTIONS;
+            float sx = 0.0f, so = 0.0f;
+#pragma unroll
+            for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
+                const Frag& f = xa[i][p * F::STEPS_PER_PORTION + st];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = DtOps<DT>::to_f32(static_cast<uint16_t>(f.v[e >> 1] >> (16 * (e & 1))));
+                    sx += xv;
+                    so = __fmaf_rn(xv, slot_off<DT, BITS, GS>(e), so);
+                }
+            }
+            sx += __shfl_xor(sx, 16, 64);
+            sx += __shfl_xor(sx, 32, 64);
+            so += __shfl_xor(so, 16, 64);
+            so += __shfl_xor(so, 32, 64);
+            ux[u] = sx;
+            uo[u] = so;
         }
-        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            uint32_t hx[2], lx[2], ho[2], lo[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = e + h;
+                const float vx = (u < NU && jj == 0) ? ux[u < NU ? u : 0] : 0.0f;
+                const float vo = (u < NU && jj == 0) ? uo[u < NU ? u : 0] : 0.0f;
+                hx[h] = DtOps<DT>::rne(vx);
+                lx[h] = DtOps<DT>::rne(vx - DtOps<DT>::to_f32(static_cast<uint16_t>(hx[h])));
+                ho[h] = DtOps<DT>::rne(vo);
+                lo[h] = DtOps<DT>::rne(vo - DtOps<DT>::to_f32(static_cast<uint16_t>(ho[h])));
+            }
+            xhi.v[e / 2] = hx[0] | (hx[1] << 16);
+            xlo.v[e / 2] = lx[0] | (lx[1] << 16);
+            ohi.v[e / 2] = ho[0] | (ho[1] << 16);
+            olo.v[e / 2] = lo[0] | (lo[1] << 16);
+        }
     }
-    // A fragment of k-block i, step s: base + i*KBLK + step_off(s); the
-    // per-quarter and per-step parts of the source position are separable.
-    const uint16_t* a_base =
-        xs_lds + static_cast<int64_t>(c < M ? c : M) * xstride + kb0 * F::KBLK + F::src_lane(0, jj) * F::SEG +
-        F::src_slot(0, jj) * 8;
-    auto a_frag = [&](int i, int s) -> Frag {
-        const int off = i * F::KBLK + (F::src_lane(s, 0) - F::src_lane(0, 0)) * F::SEG +
-                        (F::src_slot(s, 0) - F::src_slot(0, 0)) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(a_base + off);
-        return Frag{{v.x, v.y, v.z, v.w}};
-    };
-    const Frag ones = {{F::ONES, F::ONES, F::ONES, F::ONES}};
     const UnpackConsts uk = unpack_consts<DT>();
 
-    auto scale_bias = [&](const Regs& r, int i, int p, float& sc, float& bi) {
-        uint32_t sv, bv;
+    // 16-bit scale or bias of unit (portion p of k-block i) of this wavefront
+    auto unit_value = [&](const Regs& r, bool want_scale, int i, int p) -> uint32_t {
         if constexpr (VEC) {
-            const int gi = (i * F::KBLK + p * (F::KBLK / F::PORTIONS)) / GS;  // compile-time after unrolling
-            sv = r.sb.s[gi >> 1] >> (16 * (gi & 1));
-            bv = r.sb.b[gi >> 1] >> (16 * (gi & 1));
+            const int gi = (i * F::KBLK + p * F::PC) / GS;  // compile-time after unrolling
+            const uint32_t w = want_scale ? r.sb.s[gi >> 1] : r.sb.b[gi >> 1];
+            return (w >> (16 * (gi & 1))) & 0xFFFFu;
         } else {
-            sv = r.sb.s[i][p];
-            bv = r.sb.b[i][p];
+            return (want_scale ? r.sb.s[i][p] : r.sb.b[i][p]) & 0xFFFFu;
         }
-        sc = DtOps<DT>::to_f32(static_cast<uint16_t>(sv));
-        bi = DtOps<DT>::to_f32(static_cast<uint16_t>(bv));
+    };
+    // B operand of the unit products: lane (column c, quarter 0) holds the
+    // values of units 0..NU-1; the other quarters are zero.
+    auto unit_frag = [&](const Regs& r, bool want_scale) -> Frag {
+        Frag f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int u0 = 2 * v, u1 = u0 + 1;
+            const uint32_t lo16 = u0 < NU ? unit_value(r, want_scale, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
+            const uint32_t hi16 = u1 < NU ? unit_value(r, want_scale, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
+            f.v[v] = jj == 0 ? (lo16 | (hi16 << 16)) : 0u;
+        }
+        return f;
     };
 
     int parity = 0;
@@ -409,36 +525,44 @@ __global__ __launch_bounds__(64 * W, (KPW <= 4 ? 4 : 2)) void mfma_reg_kernel(
 #pragma unroll
             for (int p = 0; p < F::PORTIONS; ++p) {
                 float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                float4_t xsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
                     const int s = p * F::STEPS_PER_PORTION + st;
-                    const Frag xa = a_frag(i, s);
-                    acc = mfma<DT>(xa, bw[s], acc);
-                    xsum = mfma<DT>(xa, ones, xsum);
+                    acc = mfma<DT>(xa[i][s], bw[s], acc);
                 }
-                float sc, bi;
-                scale_bias(r, i, p, sc, bi);
-                const float bp = __fmaf_rn(-F::OFF, sc, bi);
+                const float sc = DtOps<DT>::to_f32(static_cast<uint16_t>(unit_value(r, true, i, p)));
 #pragma unroll
-                for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], __fmaf_rn(bp, xsum[q], yacc[q]));
+                for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
             }
         }
+        // unit products: + sum_u b_u X_u - sum_u s_u O_u
+        const Frag bb = unit_frag(r, false);
+        yacc = mfma<DT>(xhi, bb, yacc);
+        yacc = mfma<DT>(xlo, bb, yacc);
+        if constexpr (F::HAS_OFF) {
+            Frag sn = unit_frag(r, true);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sn.v[v] ^= 0x80008000u;  // -s, exact
+            yacc = mfma<DT>(ohi, sn, yacc);
+            yacc = mfma<DT>(olo, sn, yacc);
+        }
         // Combine the wavefronts' partial sums: every wavefront writes its
-        // partial to the buffer of this tile's parity; after one barrier
-        // wavefronts 0..3 each sum one of the four D rows a lane holds and
-        // store it.  The next tile writes the other buffer, and the tile
-        // after that can only write this one after passing the next
-        // barrier, which the reducing wavefronts reach only after reading.
-        float* rb = red + parity * (W * 64 * 4);
-        *reinterpret_cast<float4_t*>(rb + (wave * 64 + lane) * 4) = yacc;
+        // partial to the buffer of this tile's parity (layout [w][q][lane],
+        // conflict-free); after one barrier wavefronts 0..3 each sum one of
+        // the four D rows a lane holds and store it.  The next tile writes
+        // the other buffer, and the tile after that can only write this one
+        // after passing the next barrier, which the reducing wavefronts
+        // reach only after reading.
+        float* rb = red + parity * (W * 4 * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rb[(wave * 4 + q) * 64 + lane] = yacc[q];
         __syncthreads();
         if (wave < 4) {
             const int q = wave;
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) v += rb[(w * 64 + lane) * 4 + q];
-            const int64_t col = t * 16 + c;
+            for (int w = 0; w < W; ++w) v += rb[(w * 4 + q) * 64 + lane];
+            const int64_t col = tile_col0(t) + c;
             const int row = 4 * jj + q;
             if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
         }
@@ -450,6 +574,9 @@ __global__ __launch_bounds__(64 * W, (KPW <= 4 ? 4 : 2)) void mfma_reg_kernel(
 #pragma unroll
         for (int u = 0; u <= LA; ++u) {
             load_tile(min(tile + LA * step, ntiles - 1), buf[(u + LA) % (LA + 1)]);
+            // keep the prefetch ahead of the compute: left alone, the
+            // scheduler sinks these loads past it to shorten live ranges
+            __builtin_amdgcn_sched_barrier(0);
             compute_store(tile, buf[u]);
             tile += step;
             if (tile >= ntiles) break;
@@ -477,8 +604,11 @@ static_assert(separable_sources<0, 4, 32>() && separable_sources<0, 4, 64>() && 
                   separable_sources<0, 8, 128>(),
               "fragment source positions must be separable");
 
-// Launch shape: waves per workgroup, k-blocks per wavefront (W*KPW k-blocks
-// cover K), whether the scale/bias vectors can be loaded whole.
+// Launch shape: waves per workgroup and k-blocks per wavefront (W*KPW
+// k-blocks cover K), and whether the scale/bias vectors can be loaded whole.
+// The activation fragments of KPW k-blocks live in registers, so KPW stays
+// small: 16 wavefronts cover K = 4096 at two (4-bit) or four (6/8-bit)
+// k-blocks each.
 struct RegShape {
     int W, KPW;
     bool vec;
@@ -489,16 +619,18 @@ inline int64_t kblk_of(int bits) { return bits == 4 ? 128 : 64; }
 inline bool pick_shape(int bits, int gs, int64_t K, RegShape& s) {
     const int64_t kblk = kblk_of(bits);
     const int64_t nkb = (K + kblk - 1) / kblk;
-    // 8 wavefronts (two per SIMD); the smallest KPW that covers K.  The x
-    // fragments of a wavefront's k-blocks stay in registers, which bounds K.
-    for (int KPW : {1, 2, 4, 8}) {
-        if (8 * KPW >= nkb) {
-            const int64_t G = K / gs;
-            const int64_t ng = (KPW * kblk + gs - 1) / gs;
-            const int64_t vec_vals = ng >= 8 ? 8 : ng;  // 16-bit values per vector load
-            s = {8, KPW, 8 * KPW == nkb && KPW * kblk % gs == 0 && G % vec_vals == 0 && ng % 2 == 0};
-            return true;
-        }
+    static const int shapes[][2] = {{4, 1}, {8, 1}, {16, 1}, {16, 2}, {16, 4}};
+    for (const auto& sh : shapes) {
+        const int W = sh[0], KPW = sh[1];
+        if (bits == 4 && KPW > 2) continue;  // 4-bit fragments of 4 k-blocks exceed the register budget
+        if (static_cast<int64_t>(W) * KPW < nkb) continue;
+        const int64_t portions = kblk / gs > 1 ? kblk / gs : 1;
+        if (KPW * portions > 8) continue;  // unit products: at most 8 units per wavefront
+        const int64_t G = K / gs;
+        const int64_t ng = (KPW * kblk + gs - 1) / gs;
+        const int64_t vec_vals = ng >= 8 ? 8 : ng;  // 16-bit values per vector load
+        s = {W, KPW, W * KPW == nkb && KPW * kblk % gs == 0 && G % vec_vals == 0 && ng % 2 == 0};
+        return true;
     }
     return false;
 }
@@ -506,15 +638,14 @@ inline bool pick_shape(int bits, int gs, int64_t K, RegShape& s) {
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
 hipError_t launch_shape(const MatmulArgs& a) {
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t KC = static_cast<int64_t>(W) * KPW * (BITS == 4 ? 128 : 64);
-    const size_t lds = static_cast<size_t>(lds_x_bytes(a.M, KC) + lds_red_bytes(W));
-    // up to two resident workgroups per CU on 256 CUs; each walks several tiles
-    const int64_t grid = ntiles < 512 ? ntiles : 512;
-    constexpr int LA = 1;
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, LA>), dim3(static_cast<unsigned>(grid)),
-                       dim3(64 * W), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
-                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
-                       static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
+    const size_t lds = static_cast<size_t>(lds_red_bytes(W));
+    // workgroups resident at once on 256 CUs (16 wavefronts per CU); each walks several tiles
+    const int64_t resident = 256 * (16 / W);
+    const int64_t grid = ntiles < resident ? ntiles : resident;
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC>), dim3(static_cast<unsigned>(grid)), dim3(64 * W),
+                       lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
+                       static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
+                       a.K);
     return hipGetLastError();
 }
 
@@ -522,28 +653,31 @@ template <int DT, int BITS, int GS>
 hipError_t launch_reg_t(const MatmulArgs& a) {
     RegShape s;
     if (!pick_shape(BITS, GS, a.K, s)) return hipErrorInvalidValue;
-    switch (s.KPW * 2 + (s.vec ? 1 : 0)) {
-        case 2: return launch_shape<DT, BITS, GS, 8, 1, false>(a);
-        case 3: return launch_shape<DT, BITS, GS, 8, 1, true>(a);
-        case 4: return launch_shape<DT, BITS, GS, 8, 2, false>(a);
-        case 5: return launch_shape<DT, BITS, GS, 8, 2, true>(a);
-        case 8: return launch_shape<DT, BITS, GS, 8, 4, false>(a);
-        case 9: return launch_shape<DT, BITS, GS, 8, 4, true>(a);
-        case 16: return launch_shape<DT, BITS, GS, 8, 8, false>(a);
-        case 17: return launch_shape<DT, BITS, GS, 8, 8, true>(a);
+    switch (s.W * 100 + s.KPW * 2 + (s.vec ? 1 : 0)) {
+        case 402: return launch_shape<DT, BITS, GS, 4, 1, false>(a);
+        case 403: return launch_shape<DT, BITS, GS, 4, 1, true>(a);
+        case 802: return launch_shape<DT, BITS, GS, 8, 1, false>(a);
+        case 803: return launch_shape<DT, BITS, GS, 8, 1, true>(a);
+        case 1602: return launch_shape<DT, BITS, GS, 16, 1, false>(a);
+        case 1603: return launch_shape<DT, BITS, GS, 16, 1, true>(a);
+        case 1604: return launch_shape<DT, BITS, GS, 16, 2, false>(a);
+        case 1605: return launch_shape<DT, BITS, GS, 16, 2, true>(a);
+        case 1608:
+            if constexpr (BITS != 4) return launch_shape<DT, BITS, GS, 16, 4, false>(a);
+            return hipErrorInvalidValue;
+        case 1609:
+            if constexpr (BITS != 4) return launch_shape<DT, BITS, GS, 16, 4, true>(a);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool mfma_reg_supports(int bits, int64_t M, int64_t K) {
+bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K) {
     if (M > 16) return false;
     RegShape s;
-    if (!pick_shape(bits, 128, K, s)) return false;
-    // staged activations plus the reduction buffers must fit the 160 KiB of LDS
-    const int64_t KC = static_cast<int64_t>(s.W) * s.KPW * kblk_of(bits);
-    return lds_x_bytes(M, KC) + lds_red_bytes(s.W) <= 160 * 1024;
+    return pick_shape(bits, gs, K, s);
 }
 
 hipError_t launch_mfma_reg(const MatmulArgs& a) {
