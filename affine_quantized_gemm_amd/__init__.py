@@ -30,6 +30,7 @@ _DT = {torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
 EXPORTS = (
     "qmm_quantize", "qmm_dequantize", "qmm_small_m", "qmm_small_m_forced",
     "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
+    "qmm_probe_stream_read", "qmm_probe_copy",
 )
 
 
@@ -55,6 +56,8 @@ def _load():
         "qmm_packed_words": (i64, [i32, i64]),
         "qmm_strerror": (ctypes.c_char_p, [i32]),
         "qmm_kernel_name": (ctypes.c_char_p, [i32]),
+        "qmm_probe_stream_read": (i32, [vp, i64, vp, i32, vp]),
+        "qmm_probe_copy": (i32, [vp, vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -73,6 +76,8 @@ qmm_small_m_forced = _lib.qmm_small_m_forced
 qmm_select_kernel = _lib.qmm_select_kernel
 qmm_packed_words = _lib.qmm_packed_words
 qmm_kernel_supported = _lib.qmm_kernel_supported
+qmm_probe_stream_read = _lib.qmm_probe_stream_read
+qmm_probe_copy = _lib.qmm_probe_copy
 
 
 def strerror(status: int) -> str:
@@ -147,6 +152,26 @@ def dequantize(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bit
     _check(qmm_dequantize(_dt(scales.dtype), bits, group_size, N, K, wq.data_ptr(), scales.data_ptr(),
                           biases.data_ptr(), out.data_ptr(), _stream(stream)), "qmm_dequantize")
     return out
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int = 0, stream=None):
+    """Stream ``src`` (whole tensor) through a read-only kernel (measurement helper)."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < 1024:
+        raise ValueError("sink must hold 256 uint32")
+    _check(qmm_probe_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), grid,
+                                 _stream(stream)), "qmm_probe_stream_read")
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """dst <- src byte for byte (measurement helper; equal byte sizes)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst differ in size")
+    _check(qmm_probe_copy(src.data_ptr(), dst.data_ptr(), nb, _stream(stream)), "qmm_probe_copy")
 
 
 def small_m(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,

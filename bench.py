@@ -1,20 +1,30 @@
-"""Benchmark: effective weight GB/s and us/call of the verify-shape QMM.
+"""Benchmark: effective weight GB/s and us/call of the affine-quantized
+small-M matmul y[M,N] = x[M,K] . dequant(Wq[N,K])^T on one GPU.
 
-Workload (default): the verify shapes M = 4 and M = 6 with K = N = 4096
-(a q/o-projection shape), 4-bit codes, group size 64, fp16 activations
-~N(0, 1), weights ~N(0, 0.02).  A stack of distinct quantized matrices,
-more than twice the 256 MiB Infinity Cache, is cycled call by call so the
-weights stream from HBM.  One step = one call per matrix of the stack at
-M = 4, then one per matrix at M = 6.
+Workload (default ``verify``): the verify shapes M = 4 and M = 6 with
+K = N = 4096 (a q/o-projection shape), 4-bit codes, group size 64, fp16
+activations ~N(0, 1), weights ~N(0, 0.02).  A stack of distinct quantized
+matrices, more than twice the 256 MiB Infinity Cache, is cycled call by call
+so the weights stream from HBM.  One step = one call per matrix of the stack
+at M = 4, then one per matrix at M = 6.  Other workloads (``--workload``)
+are the batched-decode shapes and the wide LM head.
 
-Metric: effective weight GB/s = (packed weight bytes + 4 bytes of scale/bias
-per group) / time per call, GB = 1e9 bytes -- the byte count of the MLX
-issue #4720 reproducer ("To Reproduce").  Printed as one JSON line.
+Metric: effective weight GB/s = (packed weight bytes + 4 bytes of scale and
+bias per group) / time per call, GB = 1e9 bytes -- the byte count of the
+MLX issue #4720 reproducer ("To Reproduce").  Printed as one JSON line.
+
+Counter post-processing (no GPU): ``bench.py --traffic-from FETCH_DIR
+WRITE_DIR`` reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
+runs of this script, scales the matmul kernel's counters by what the same
+counters read for the copy-kernel dispatch of known size that every run
+makes, and writes ``profiles/traffic_<workload>.json``.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -25,11 +35,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-INFINITY_CACHE = 256 << 20
+COPY_CAL_BYTES = 64 << 20      # copy-kernel dispatch used to scale byte counters
 
 
 def weight_bytes(N, K, bits, gs):
     return N * K * bits // 8 + 4 * N * (K // gs)
+
+
+def alg_bytes(M, N, K, bits, gs):
+    """Bytes one call must move: packed weights + scale/bias + x + y."""
+    return weight_bytes(N, K, bits, gs) + 2 * M * K + 2 * M * N
 
 
 WORKLOADS = {
@@ -53,6 +68,10 @@ def parse():
     p.add_argument("--kernel", type=int, default=None, help="force a kernel variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the graph-replay and streaming-read measurements")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="post-process two rocprofv3 --pmc runs of this script (no GPU)")
     return p.parse_args()
 
 
@@ -66,8 +85,8 @@ def kernel_source_digest():
 
 
 def load_traffic(workload, digest):
-    """HBM traffic per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel sources."""
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -78,8 +97,88 @@ def load_traffic(workload, digest):
     return t.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------- counters
+
+def _is_copy_probe(name):
+    return name.startswith("(anonymous namespace)::copy_kernel(")
+
+
+def _is_matmul_kernel(name):
+    return name.startswith("void qmm::") and "quantize_kernel" not in name
+
+
+def _read_counter_dir(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per_kernel, copies = {}, []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name, v = row["Kernel_Name"], float(row["Counter_Value"])
+                if _is_copy_probe(name):
+                    copies.append(v)
+                elif _is_matmul_kernel(name):
+                    per_kernel.setdefault(name, []).append(v)
+    if not copies or not per_kernel:
+        raise SystemExit(f"{d}: missing copy or matmul dispatches for {counter}")
+    name = max(per_kernel, key=lambda k: len(per_kernel[k]))
+    vals = per_kernel[name]
+    return name, sum(vals) / len(vals), len(vals), sum(copies) / len(copies)
+
+
+def _bench_line(d):
+    for fn in glob.glob(os.path.join(d, "*.log")) + glob.glob(os.path.join(d, "*.json")):
+        with open(fn) as f:
+            for line in f:
+                if line.startswith("{") and '"metric"' in line:
+                    return json.loads(line)
+    raise SystemExit(f"no bench JSON line in {d}")
+
+
+def traffic_from(fetch_dir, write_dir):
+    bf, bw = _bench_line(fetch_dir), _bench_line(write_dir)
+    if bf["kernel_source_digest"] != bw["kernel_source_digest"] or bf["config"] != bw["config"]:
+        raise SystemExit("the two counter runs used different sources or workloads")
+    kf, fetch_kib, nf, copy_fetch_kib = _read_counter_dir(fetch_dir, "FETCH_SIZE")
+    kw, write_kib, nw, copy_write_kib = _read_counter_dir(write_dir, "WRITE_SIZE")
+    if kf != kw:
+        raise SystemExit(f"different dominant kernels: {kf} vs {kw}")
+    f_scale = COPY_CAL_BYTES / (copy_fetch_kib * 1024.0)
+    w_scale = COPY_CAL_BYTES / (copy_write_kib * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    wl = bf["config"]["workload_name"]
+    out = {
+        "workload": wl,
+        "kernel": kf,
+        "kernel_source_digest": bf["kernel_source_digest"],
+        "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "fetch_kib_per_launch_raw": round(fetch_kib, 1),
+        "write_kib_per_launch_raw": round(write_kib, 1),
+        "copy_calibration": {"bytes": COPY_CAL_BYTES, "fetch_kib": copy_fetch_kib, "write_kib": copy_write_kib,
+                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "fetch_bytes_per_launch": int(fetch_b),
+        "write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+        "alg_bytes_per_launch": bf["roofline"]["alg_bytes_per_launch"],
+        "traffic_over_alg": round((fetch_b + write_b) / bf["roofline"]["alg_bytes_per_launch"], 4),
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------- oracle leg
+
 def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
-    """The oracle, untuned, on one matrix of the workload (host cores)."""
+    """The oracle, untuned, on one matrix of the workload (host cores).  For
+    the LM head only a slice of the output columns is computed, scaled to a
+    per-call figure (columns are independent)."""
     import numpy as np
     import synth
     from oracle import qmm_oracle as O
@@ -88,7 +187,8 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    w = synth.to_oracle(synth.normal((N, K), 0.02, dt, 9000))
+    Ns = min(N, 16384)
+    w = synth.to_oracle(synth.normal((Ns, K), 0.02, dt, 9000))
     wq, sc, bi = O.quantize(w, dt, bits, gs)
     xs = {M: synth.to_oracle(synth.normal((M, K), 1.0, dt, 9100 + M)) for M in Ms}
     calls = 0
@@ -100,15 +200,86 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
-    per_call = el / calls
-    return {"value": weight_bytes(N, K, bits, gs) / per_call / 1e9, "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{calls} oracle calls (M in {list(Ms)}) on one {N}x{K} matrix, {el:.1f} s; "
-                      f"{per_call * 1e6:.0f} us/call"}
+    per_call = el / calls * (N / Ns)
+    sample = (f"{calls} oracle calls (M in {list(Ms)}) on one {Ns}x{K} matrix"
+              + (f" ({Ns} of the {N} output columns, time scaled by {N / Ns:.2f})" if Ns < N else "")
+              + f", {el:.1f} s; {per_call * 1e6:.0f} us per full call")
+    return {"value": round(weight_bytes(N, K, bits, gs) / per_call / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle", "sample": sample,
+            "us_per_call": round(per_call * 1e6, 1)}
+
+
+# ---------------------------------------------------------------- GPU legs
+
+def graph_us_per_call(torch, Q, stack, x, y, bits, gs, kernel, reps):
+    """The same call sequence captured once into a HIP graph and replayed
+    (host launch cost removed)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for (wq, sc, bi) in stack:          # warm-up on the capture stream
+            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kernel)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for (wq, sc, bi) in stack:
+            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kernel)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(stack))
+
+
+def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
+    """A plain coalesced read of B bytes per launch, cycling a pool the size
+    of the weight stack: what any kernel streaming B bytes can reach here."""
+    B16 = B // 16 * 16
+    n = max(1, stack_bytes // B16)
+    pool = torch.empty(n * B16, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    views = [pool[i * B16:(i + 1) * B16] for i in range(n)]
+    best = None
+    for grid in (1024, 2048, 4096):
+        for v in views:
+            Q.probe_stream_read(v, sink, grid)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for v in views:
+                Q.probe_stream_read(v, sink, grid)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        if best is None or us < best[0]:
+            best = (us, grid)
+    del pool
+    return {"us_per_call": round(best[0], 3), "gbs": round(B16 / (best[0] * 1e-6) / 1e9, 1), "grid": best[1]}
+
+
+def copy_calibration(torch, Q):
+    """One copy-kernel dispatch of COPY_CAL_BYTES (its byte counters scale
+    the matmul kernel's in counter runs); checked for correctness."""
+    src = torch.arange(COPY_CAL_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    Q.probe_copy(src, dst)
+    torch.cuda.synchronize()
+    if not torch.equal(src, dst):
+        raise RuntimeError("probe copy mismatch")
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the per-GPU path would be sharded by output columns with no collective).", file=sys.stderr)
@@ -136,53 +307,59 @@ def main():
     ys = {M: torch.empty((M, N), dtype=tdt, device=dev) for M in Ms}
     torch.cuda.synchronize()
 
-    def step():
-        for M in Ms:
-            x, y = xs[M], ys[M]
-            for (wq, sc, bi) in stack:
-                Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
+    def calls(M):
+        x, y = xs[M], ys[M]
+        for (wq, sc, bi) in stack:
+            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
 
     for _ in range(args.warmup):
-        step()
+        for M in Ms:
+            calls(M)
     torch.cuda.synchronize()
 
-    # per-M timing (us/call), events on the stream the kernels run on
-    per_m = {}
-    for M in Ms:
-        x, y = xs[M], ys[M]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, 2 * args.steps)
-        e0.record(stream)
-        for _ in range(reps):
-            for (wq, sc, bi) in stack:
-                Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_m[M] = e0.elapsed_time(e1) * 1e3 / (reps * S)
-
-    # ---- timed steps
+    # ---- timed steps; events around each M block give per-launch durations
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in Ms]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for s in range(args.steps):
+        for j, M in enumerate(Ms):
+            ev[s][j][0].record(stream)
+            calls(M)
+            ev[s][j][1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1)
-    calls = args.steps * S * len(Ms)
-    us_call = ms * 1e3 / calls
-    gbs = B * calls / (ms * 1e-3) / 1e9
+    ms = e_start.elapsed_time(e_end)
+    per_m = {M: sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) * 1e3
+             / (args.steps * S) for j, M in enumerate(Ms)}
+    ncalls = args.steps * S * len(Ms)
+    gbs = B * ncalls / (ms * 1e-3) / 1e9
 
-    # roofline of the dominant kernel: algorithmic bytes (weights + x + y) per launch
-    alg = {M: B + 2 * M * K + 2 * M * N for M in Ms}
+    # ---- roofline of the matmul kernel: algorithmic bytes / mean launch duration
+    alg = {M: alg_bytes(M, N, K, bits, gs) for M in Ms}
     alg_mean = sum(alg.values()) / len(Ms)
-    achieved = sum(alg[M] / (per_m[M] * 1e-6) for M in Ms) / len(Ms) / 1e9
+    launch_us = sum(per_m.values()) / len(Ms)
+    achieved = alg_mean / (launch_us * 1e-6) / 1e9
     digest = kernel_source_digest()
     kid = args.kernel if args.kernel is not None else Q.select_kernel(tdt, bits, gs, Ms[-1], N, K)
+    kernels = {f"M{M}": Q.kernel_name(args.kernel if args.kernel is not None
+                                      else Q.select_kernel(tdt, bits, gs, M, N, K)) for M in Ms}
+
+    extras = {}
+    if not args.no_extras:
+        extras["graph_us_per_call"] = {
+            f"M{M}": round(graph_us_per_call(torch, Q, stack, xs[M], ys[M], bits, gs, args.kernel,
+                                             max(2, args.steps // 2)), 3) for M in Ms}
+        extras["stream_read_ceiling"] = stream_read_ceiling(torch, Q, B, S * B, max(2, args.steps // 2))
+    copy_calibration(torch, Q)
+
     out = {
-        "metric": "effective weight GB/s of the verify-shape affine-quantized QMM (M=4 and M=6)",
+        "metric": "effective weight GB/s of the affine-quantized small-M QMM "
+                  "((packed weight + scale/bias bytes) / time per call)",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -196,14 +373,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: M in {list(Ms)}, K={K}, N={N}, {bits}-bit, group {gs}, {dt}; "
                                f"{S} distinct matrices ({S * B / 2**20:.0f} MiB) cycled per call",
+                   "workload_name": args.workload,
                    "M": list(Ms), "N": N, "K": K, "bits": bits, "group_size": gs, "stack": S,
-                   "kernel": Q.kernel_name(kid)},
+                   "kernel": kernels},
         "us_per_call": {f"M{M}": round(per_m[M], 3) for M in Ms},
         "weight_gbs_per_m": {f"M{M}": round(B / (per_m[M] * 1e-6) / 1e9, 1) for M in Ms},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload, digest),
-                     "alg_bytes_per_launch": int(alg_mean), "kernel": Q.kernel_name(kid)},
+                     "alg_bytes_per_launch": int(alg_mean), "launch_us": round(launch_us, 3),
+                     "kernel": Q.kernel_name(kid)},
+        **extras,
+        "kernel_source_digest": digest,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

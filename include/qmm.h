@@ -137,6 +137,27 @@ const char* qmm_strerror(int status);
 /* Static name of a kernel variant ("?" if unknown). */
 const char* qmm_kernel_name(int kernel_id);
 
+/*
+ * Measurement helpers (not part of the matmul path).
+ *
+ * qmm_probe_stream_read: read `bytes` (a multiple of 16) from device memory
+ * `src` with coalesced 16-byte nontemporal loads, `grid` workgroups of 256
+ * threads (0 = 2048; never more than the data needs), and discard the data.
+ * `sink` is caller-owned device memory of at least 256 uint32 that the
+ * kernel may write (practically never does).  It is the streaming-read
+ * ceiling a matmul streaming the same bytes can approach.
+ *
+ * qmm_probe_copy: copy `bytes` (a multiple of 16) from `src` to `dst`
+ * (device memory, not overlapping).  It reads and writes exactly `bytes`
+ * each, so hardware byte counters taken on it give their scale.
+ *
+ * Both: 16-byte aligned pointers (QMM_ERR_MISALIGNED otherwise), negative
+ * sizes -> QMM_ERR_INVALID_ARG, other sizes -> QMM_ERR_UNSUPPORTED, 0 bytes
+ * -> QMM_OK with nothing launched; asynchronous on `stream` like the rest.
+ */
+int qmm_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, void* stream);
+int qmm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,3 +129,17 @@ def test_select_kernel_is_total_over_supported_shapes():
                         assert k in Q.KERNEL_IDS, (dt, bits, gs, M, N, K, k)
     assert Q.select_kernel(torch.float16, 4, 64, 65, 64, 256) == Q.QMM_ERR_UNSUPPORTED
     assert Q.select_kernel(torch.float16, 4, 64, -1, 64, 256) == Q.QMM_ERR_INVALID_ARG
+
+
+def test_probe_validation():
+    assert Q.qmm_probe_stream_read(A, -16, A, 0, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(A, 24, A, 0, None) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_probe_stream_read(None, 64, A, 0, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(A, 64, None, 0, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(MIS, 64, A, 0, None) == Q.QMM_ERR_MISALIGNED
+    assert Q.qmm_probe_stream_read(A, 64, A, -1, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(None, 0, None, 0, None) == Q.QMM_OK
+    assert Q.qmm_probe_copy(A, A, 8, None) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_probe_copy(A, MIS, 64, None) == Q.QMM_ERR_MISALIGNED
+    assert Q.qmm_probe_copy(A, None, 64, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_copy(None, None, 0, None) == Q.QMM_OK
