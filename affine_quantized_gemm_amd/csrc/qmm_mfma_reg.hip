@@ -327,7 +327,33 @@ __host__ __device__ constexpr float slot_off(int e) {
     }
 }
 
-__host__ __device__ inline int64_t lds_red_bytes(int W) { return 2LL * W * 64 * 4 * 4; }
+// 16-bit patterns of the few exact constants the unit sums use (1 and the
+// code offsets 0, 64, 128, 1024).
+template <int DT>
+struct DtBits;
+template <>
+struct DtBits<DT_F16> {
+    static constexpr uint32_t one = 0x3C00u;
+    __host__ __device__ static constexpr uint32_t of(float v) {
+        return v == 1024.0f ? 0x6400u : v == 64.0f ? 0x5400u : v == 128.0f ? 0x5800u : v == 1.0f ? 0x3C00u : 0u;
+    }
+};
+template <>
+struct DtBits<DT_BF16> {
+    static constexpr uint32_t one = 0x3F80u;
+    __host__ __device__ static constexpr uint32_t of(float v) {
+        return v == 1024.0f ? 0x4480u : v == 64.0f ? 0x4280u : v == 128.0f ? 0x4300u : v == 1.0f ? 0x3F80u : 0u;
+    }
+};
+
+// LDS of one wavefront: its activation rows for its part of K (row stride
+// padded by 16 bytes so that rows fall in different banks), staged once; the
+// first 2 KB later hold its two partial-tile buffers (parities).
+__host__ __device__ constexpr int xs_row_elems(int kpw, int kblk) { return kpw * kblk + 8; }
+__host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
+    const int x = M * xs_row_elems(kpw, kblk) * 2;
+    return x > 2048 ? x : 2048;
+}
 
 // W wavefronts per workgroup; wavefront w owns the KPW consecutive k-blocks
 // [w*KPW, (w+1)*KPW) of K.  One workgroup owns a tile of 16 columns at a
@@ -353,7 +379,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     static_assert(NU <= 8, "the unit products use the first k-slot quarter only");
     using Regs = TileRegs<VEC, NGW, KPW, F::SEG_WORDS, F::PORTIONS>;
     extern __shared__ __align__(16) uint8_t lds[];
-    float* red = reinterpret_cast<float*>(lds);
+    constexpr int XS_ROW = xs_row_elems(KPW, F::KBLK);
+    const int wave_lds = wave_lds_bytes(M, KPW, F::KBLK);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -414,26 +441,45 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         }
     };
 
-    // ---- prologue: this wavefront's activation fragments first (rows >= M
-    // and positions >= K read nothing and stay zero), then the first tile
-    uint4 xraw[KPW][F::STEPS];
+    // ---- prologue.  This wavefront's activation rows [0, M) x its part of
+    // K are read with coalesced 16-byte loads (whole lines, every lane busy)
+    // ahead of the first tile's weights, then staged through its own LDS
+    // region and read back in fragment order.  Positions >= K are zero.
+    constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
+    constexpr int XG = (16 * CPR + 63) / 64;
+    uint4 xg[XG];
     {
-        const bool row_ok = c < M;
-        const uint16_t* xrow = x + static_cast<int64_t>(row_ok ? c : 0) * K;
 #pragma unroll
-        for (int i = 0; i < KPW; ++i)
-#pragma unroll
-            for (int s = 0; s < F::STEPS; ++s) {
-                const int64_t k0 = (kb0 + i) * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-                xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
-                if (row_ok && (VEC || k0 < K)) xraw[i][s] = *reinterpret_cast<const uint4*>(xrow + k0);
-            }
+        for (int j = 0; j < XG; ++j) {
+            const int t = lane + 64 * j;
+            const int row = t / CPR, piece = t % CPR;
+            const int64_t k = kb0 * F::KBLK + piece * 8;
+            xg[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < M && (VEC || k < K)) xg[j] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(row) * K + k);
+        }
     }
     Regs buf[LA + 1];
     const int64_t step = gridDim.x;
     int64_t tile = blockIdx.x;
     load_tile(min(tile, ntiles - 1), buf[0]);
     __builtin_amdgcn_sched_barrier(0);
+
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
+#pragma unroll
+    for (int j = 0; j < XG; ++j) {
+        const int t = lane + 64 * j;
+        const int row = t / CPR, piece = t % CPR;
+        if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
+    }
+    uint4 xraw[KPW][F::STEPS];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int s = 0; s < F::STEPS; ++s) {
+            const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
+            xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
+            if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
+        }
 
     Frag xa[KPW][F::STEPS];
 #pragma unroll
@@ -442,33 +488,40 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         for (int s = 0; s < F::STEPS; ++s) xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
 
     // Unit sums X_u = sum x and O_u = sum x*off of row c over each unit of
-    // this wavefront: per-lane partial sums, then a sum over the four k-slot
-    // quarters (lanes c, c+16, c+32, c+48).  A operands of the unit products
-    // (split hi + lo): lane (row c, quarter 0) holds units 0..NU-1, the other
-    // quarters zero.
+    // this wavefront, on the matrix cores: with B = the activation fragment
+    // of a step (B[k][c] = x[c][k], the same register that serves as A) and
+    // A = a pattern with row u all ones and row 8 + u holding the offsets of
+    // the k-slots (u = the step's unit), one product per step accumulates
+    // D[u][c] = X_u[c] and D[8 + u][c] = O_u[c].  A lane (column c, quarter
+    // jj) receives rows 4jj..4jj+3: X_0..3, X_4..7, O_0..3, O_4..7 for
+    // jj = 0..3.  Lane (row c, quarter 0) then collects all eight of each
+    // and splits them into high and low 16-bit parts: the A operands of the
+    // unit products, whose other quarters stay zero.
     Frag xhi, xlo, ohi, olo;
     {
-        float ux[NU], uo[NU];
+        const int arow = lane & 15;  // A-operand row this lane supplies
+        float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int i = u / F::PORTIONS, p = u % F::PORTIONS;
-            float sx = 0.0f, so = 0.0f;
+            Frag e;
 #pragma unroll
-            for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
-                const Frag& f = xa[i][p * F::STEPS_PER_PORTION + st];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xv = DtOps<DT>::to_f32(static_cast<uint16_t>(f.v[e >> 1] >> (16 * (e & 1))));
-                    sx += xv;
-                    so = __fmaf_rn(xv, slot_off<DT, BITS, GS>(e), so);
-                }
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t ones = DtBits<DT>::one * 0x10001u;
+                const uint32_t offs = DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v)) |
+                                      (DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v + 1)) << 16);
+                e.v[v] = arow == u ? ones : (arow == 8 + u ? offs : 0u);
             }
-            sx += __shfl_xor(sx, 16, 64);
-            sx += __shfl_xor(sx, 32, 64);
-            so += __shfl_xor(so, 16, 64);
-            so += __shfl_xor(so, 32, 64);
-            ux[u] = sx;
-            uo[u] = so;
+#pragma unroll
+            for (int st = 0; st < F::STEPS_PER_PORTION; ++st) d = mfma<DT>(e, xa[i][p * F::STEPS_PER_PORTION + st], d);
+        }
+        float xv[8], ov[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            xv[r] = d[r];
+            xv[4 + r] = __shfl(d[r], (lane & 15) + 16, 64);
+            ov[r] = __shfl(d[r], (lane & 15) + 32, 64);
+            ov[4 + r] = __shfl(d[r], (lane & 15) + 48, 64);
         }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -476,8 +529,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int u = e + h;
-                const float vx = (u < NU && jj == 0) ? ux[u < NU ? u : 0] : 0.0f;
-                const float vo = (u < NU && jj == 0) ? uo[u < NU ? u : 0] : 0.0f;
+                const float vx = (u < NU && jj == 0) ? xv[u] : 0.0f;
+                const float vo = (u < NU && jj == 0) ? ov[u] : 0.0f;
                 hx[h] = DtOps<DT>::rne(vx);
                 lx[h] = DtOps<DT>::rne(vx - DtOps<DT>::to_f32(static_cast<uint16_t>(hx[h])));
                 ho[h] = DtOps<DT>::rne(vo);
@@ -547,21 +600,22 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             yacc = mfma<DT>(olo, sn, yacc);
         }
         // Combine the wavefronts' partial sums: every wavefront writes its
-        // partial to the buffer of this tile's parity (layout [w][q][lane],
-        // conflict-free); after one barrier wavefronts 0..3 each sum one of
-        // the four D rows a lane holds and store it.  The next tile writes
-        // the other buffer, and the tile after that can only write this one
-        // after passing the next barrier, which the reducing wavefronts
-        // reach only after reading.
-        float* rb = red + parity * (W * 4 * 64);
+        // partial to the buffer of this tile's parity at the start of its own
+        // LDS region (over its staged activations, which it has read by then;
+        // layout [q][lane], conflict-free); after one barrier wavefronts 0..3
+        // each sum one of the four D rows a lane holds and store it.  The
+        // next tile writes the other buffer, and the tile after that can only
+        // write this one after passing the next barrier, which the reducing
+        // wavefronts reach only after reading.
+        float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 256;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rb[(wave * 4 + q) * 64 + lane] = yacc[q];
+        for (int q = 0; q < 4; ++q) rb[q * 64 + lane] = yacc[q];
         __syncthreads();
         if (wave < 4) {
             const int q = wave;
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) v += rb[(w * 4 + q) * 64 + lane];
+            for (int w = 0; w < W; ++w) v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 256 + q * 64 + lane];
             const int64_t col = tile_col0(t) + c;
             const int row = 4 * jj + q;
             if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
@@ -638,10 +692,17 @@ inline bool pick_shape(int bits, int gs, int64_t K, RegShape& s) {
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
 hipError_t launch_shape(const MatmulArgs& a) {
     const int64_t ntiles = (a.N + 15) / 16;
-    const size_t lds = static_cast<size_t>(lds_red_bytes(W));
+    const size_t lds = static_cast<size_t>(W) * wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK);
     // workgroups resident at once on 256 CUs (16 wavefronts per CU); each walks several tiles
     const int64_t resident = 256 * (16 / W);
     const int64_t grid = ntiles < resident ? ntiles : resident;
+    if (lds > 65536) {
+        // above the default dynamic-LDS limit: raise it once per kernel
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (attr != hipSuccess) return attr;
+    }
     hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC>), dim3(static_cast<unsigned>(grid)), dim3(64 * W),
                        lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
                        static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
