@@ -134,7 +134,7 @@ const char* qmm_kernel_name(int kernel_id) {
     switch (kernel_id) {
         case QMM_KERNEL_VALU: return "valu_splitfree";
         case QMM_KERNEL_MFMA_REG: return "mfma_splitfree_reg";
-        case QMM_KERNEL_MFMA_LDS: return "mfma_lds";
+        case QMM_KERNEL_MFMA_PASS: return "mfma_splitfree_pass";
         default: return "?";
     }
 }

@@ -25,6 +25,7 @@ struct MatmulArgs {
 
 hipError_t launch_valu(const MatmulArgs& a);
 hipError_t launch_mfma_reg(const MatmulArgs& a);
+hipError_t launch_mfma_pass(const MatmulArgs& a);
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K);
 
 }  // namespace qmm

@@ -79,7 +79,7 @@ enum qmm_status {
 enum qmm_kernel {
     QMM_KERNEL_VALU = 0,      /* split-free, VALU dot products, cross-lane K reduction */
     QMM_KERNEL_MFMA_REG = 1,  /* split-free, MFMA with in-register weight fragments, M <= 16 */
-    QMM_KERNEL_MFMA_LDS = 2,  /* weights dequantized to LDS, MFMA, any M <= 64 */
+    QMM_KERNEL_MFMA_PASS = 2, /* split-free, MFMA, K walked in passes of 16 k-blocks, any K, M <= 64 */
     QMM_KERNEL_COUNT = 3
 };
 
@@ -113,7 +113,7 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
 
 /* As qmm_small_m with the variant forced (measurement and tests).
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
- * (QMM_KERNEL_MFMA_REG needs M <= 16). */
+ * (QMM_KERNEL_MFMA_REG needs M <= 16 and K <= 4096). */
 int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
                        const void* x, const uint32_t* wq, const void* scales,
                        const void* biases, void* y, void* stream, int kernel_id);

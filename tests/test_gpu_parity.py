@@ -191,3 +191,17 @@ def test_errors_raise(Q):
     with pytest.raises(Q.QmmError) as e:
         Q.small_m(torch.ones((65, 256), dtype=torch.float16, device="cuda"), wq, sc, bi, 4, 64)
     assert e.value.status == Q.QMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("K", [2112, 4160, 8256])
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 4, 64), ("bf16", 4, 32), ("f16", 6, 128), ("bf16", 8, 64),
+                                        ("f16", 8, 32), ("bf16", 6, 64)])
+def test_pass_kernel_multipass(Q, K, dt, bits, gs):
+    """K walked in several passes with a partial last pass (and, at 4 bits,
+    a k-block cut by K); M across 16-row blocks; ragged N."""
+    if K % gs:
+        pytest.skip("K not a multiple of the group size")
+    for M, N in ((1, 17), (16, 300), (17, 33), (40, 129)):
+        print(f"pass {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
+        ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=K + M + bits, kernel=Q.KERNEL_MFMA_PASS)
+        assert ok, (M, N, worst)
