@@ -162,8 +162,8 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
 
     auto process = [&](int64_t it, const Regs& r) {
         const int pass = static_cast<int>(it % P);
-        // this iteration's activation block, staged at the end of the
-        // previous one, in fragment order
+        // this iteration's activation block, staged at the top of the
+        // iteration, in fragment order
         Frag xa[F::STEPS];
 #pragma unroll
         for (int s = 0; s < F::STEPS; ++s) {
@@ -247,11 +247,6 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
         }
-        // the next iteration's activation block (its loads were issued
-        // before this iteration's weights) replaces this one in LDS: this
-        // wavefront has read its fragments above, and its LDS accesses
-        // execute in order
-        stage_x();
         if (pass == P - 1) {
             // combine the wavefronts' partial tiles (parity double buffer,
             // one barrier per tile, as in the register-resident kernel)
@@ -274,15 +269,19 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
         }
     };
 
+    // Iteration cur: its activation block (loaded one iteration earlier, and
+    // issued before that iteration's weights, so waiting for it does not
+    // wait for them) goes to LDS, replacing the previous block, whose
+    // fragments this wavefront has already read (its LDS accesses execute in
+    // order); then the next iteration's loads are issued, then cur computes.
     Regs buf[2];
     load_it(0, buf[0]);
-    stage_x();
-    __builtin_amdgcn_sched_barrier(0);
     for (int64_t it = 0; it < n_it; it += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int64_t cur = it + u;
             if (cur >= n_it) break;
+            stage_x();
             load_it(cur + 1 < n_it ? cur + 1 : n_it - 1, buf[u ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
             process(cur, buf[u]);

@@ -1,0 +1,129 @@
+"""Crossover sweep of the small-M kernel variants on the current GPU.
+
+For each weight shape and each M, every variant that can run the problem is
+timed through ``qmm_small_m_forced`` on a stack of distinct quantized
+matrices larger than the Infinity Cache (so the weights stream from HBM),
+cycled call by call, replayed from a captured HIP graph and timed with HIP
+events on the replay stream.  The fastest
+variant per (shape, M) is what ``qmm_select_kernel`` should return; the
+measured table is the source of the crossovers compiled into the dispatch.
+
+    python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...]
+
+The pages' own dispatch story is a crossover curve in M, measured per shape
+(MLX issue #4720, "Root cause" and the M-sweep table under "Measurements").
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import affine_quantized_gemm_amd as Q  # noqa: E402
+import synth  # noqa: E402
+
+SHAPES = {
+    # name: (N, K, dtype, bits, group_size)
+    "verify": (4096, 4096, "f16", 4, 64),
+    "kv": (1024, 4096, "f16", 4, 64),
+    "gateup": (14336, 4096, "f16", 4, 64),
+    "down": (4096, 14336, "f16", 4, 64),
+    "lmhead": (151936, 4096, "bf16", 4, 64),
+    "verify8": (4096, 4096, "f16", 8, 64),
+    "verify6": (4096, 4096, "bf16", 6, 128),
+}
+MS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 36, 48, 64)
+
+
+def weight_bytes(N, K, bits, gs):
+    return N * K * bits // 8 + 4 * N * (K // gs)
+
+
+def time_calls(fn, n_calls, reps=5):
+    """Best per-call time of fn's launches, replayed from a HIP graph
+    captured from them (so the host's launch cost is not timed)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_calls
+        best = us if best is None else min(best, us)
+    return best
+
+
+def sweep_shape(name, ms, stack_mib):
+    N, K, dt, bits, gs = SHAPES[name]
+    tdt = synth.TORCH_DT[dt]
+    B = weight_bytes(N, K, bits, gs)
+    S = max(2, -(-(stack_mib << 20) // B))
+    stack = []
+    for i in range(S):
+        w = synth.normal((N, K), 0.02, dt, 7000 + i, device="cuda")
+        stack.append(Q.quantize(w, bits, gs))
+        del w
+    rows = []
+    for M in ms:
+        x = synth.normal((M, K), 1.0, dt, 7500 + M, device="cuda")
+        y = torch.empty((M, N), dtype=tdt, device="cuda")
+        res = {}
+        for kid in Q.KERNEL_IDS:
+            if not Q.kernel_supported(tdt, bits, gs, M, N, K, kid):
+                continue
+
+            def run(kid=kid):
+                for (wq, sc, bi) in stack:
+                    Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kid)
+
+            res[Q.kernel_name(kid)] = round(time_calls(run, len(stack)), 3)
+        best = min(res, key=res.get)
+        sel = Q.kernel_name(Q.select_kernel(tdt, bits, gs, M, N, K))
+        rows.append({"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "M": M, "us": res,
+                     "fastest": best, "selected": sel,
+                     "selected_gbs": round(B / (res[sel] * 1e-6) / 1e9, 1)})
+        print(f"{name:8s} M={M:3d}  " + "  ".join(f"{k} {v:8.2f}" for k, v in res.items())
+              + f"   fastest {best}   selected {sel}", flush=True)
+    del stack
+    torch.cuda.empty_cache()
+    return rows
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--shapes", default=",".join(SHAPES))
+    p.add_argument("--ms", default=",".join(map(str, MS)))
+    p.add_argument("--stack-mib", type=int, default=576)
+    p.add_argument("--json", default=None)
+    a = p.parse_args()
+    ms = [int(m) for m in a.ms.split(",")]
+    rows = []
+    for name in a.shapes.split(","):
+        rows += sweep_shape(name, ms, a.stack_mib)
+    if a.json:
+        with open(a.json, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

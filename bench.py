@@ -6,8 +6,11 @@ K = N = 4096 (a q/o-projection shape), 4-bit codes, group size 64, fp16
 activations ~N(0, 1), weights ~N(0, 0.02).  A stack of distinct quantized
 matrices, more than twice the 256 MiB Infinity Cache, is cycled call by call
 so the weights stream from HBM.  One step = one call per matrix of the stack
-at M = 4, then one per matrix at M = 6.  Other workloads (``--workload``)
-are the batched-decode shapes and the wide LM head.
+at M = 4, then one per matrix at M = 6, issued by replaying a HIP graph
+captured from those calls (one graph per M; the launches cost more host time
+than a verify-shape kernel runs, so issuing them one by one from Python would
+time the host).  The one-by-one rate is reported beside it.  Other workloads
+(``--workload``) are the batched-decode shapes and the wide LM head.
 
 Metric: effective weight GB/s = (packed weight bytes + 4 bytes of scale and
 bias per group) / time per call, GB = 1e9 bytes -- the byte count of the
@@ -211,34 +214,41 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
 
 # ---------------------------------------------------------------- GPU legs
 
-def graph_us_per_call(torch, Q, stack, x, y, bits, gs, kernel, reps):
-    """The same call sequence captured once into a HIP graph and replayed
-    (host launch cost removed)."""
+def capture(torch, fn):
+    """Capture fn's launches (on torch's current stream inside the capture)
+    into one HIP graph; fn runs once eagerly first on the capture stream."""
     g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for (wq, sc, bi) in stack:          # warm-up on the capture stream
-            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kernel)
-    torch.cuda.current_stream().wait_stream(s)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        for (wq, sc, bi) in stack:
-            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kernel)
+        fn()
     g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def stream_us_per_call(torch, fn, n_calls, reps):
+    """fn's launches issued one by one from Python on the current stream
+    (host launch cost included)."""
+    fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        g.replay()
+        fn()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * len(stack))
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_calls)
 
 
 def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
     """A plain coalesced read of B bytes per launch, cycling a pool the size
-    of the weight stack: what any kernel streaming B bytes can reach here."""
+    of the weight stack, replayed from a HIP graph like the timed step: what
+    any kernel streaming B bytes per launch can reach here."""
     B16 = B // 16 * 16
     n = max(1, stack_bytes // B16)
     pool = torch.empty(n * B16, dtype=torch.uint8, device="cuda")
@@ -247,14 +257,14 @@ def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
     views = [pool[i * B16:(i + 1) * B16] for i in range(n)]
     best = None
     for grid in (1024, 2048, 4096):
-        for v in views:
-            Q.probe_stream_read(v, sink, grid)
-        torch.cuda.synchronize()
+        def reads(grid=grid):
+            for v in views:
+                Q.probe_stream_read(v, sink, grid)
+        g = capture(torch, reads)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            for v in views:
-                Q.probe_stream_read(v, sink, grid)
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * n)
@@ -312,9 +322,13 @@ def main():
         for (wq, sc, bi) in stack:
             Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
 
+    # The step's launches are captured once per M into a HIP graph and the
+    # graphs are replayed: the calls are launch-bound from Python (a few us
+    # of host time each, comparable to one verify-shape kernel).
+    graphs = {M: capture(torch, lambda M=M: calls(M)) for M in Ms}
     for _ in range(args.warmup):
         for M in Ms:
-            calls(M)
+            graphs[M].replay()
     torch.cuda.synchronize()
 
     # ---- timed steps; events around each M block give per-launch durations
@@ -328,7 +342,7 @@ def main():
     for s in range(args.steps):
         for j, M in enumerate(Ms):
             ev[s][j][0].record(stream)
-            calls(M)
+            graphs[M].replay()
             ev[s][j][1].record(stream)
     e_end.record(stream)
     torch.cuda.synchronize()
@@ -351,9 +365,9 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras["graph_us_per_call"] = {
-            f"M{M}": round(graph_us_per_call(torch, Q, stack, xs[M], ys[M], bits, gs, args.kernel,
-                                             max(2, args.steps // 2)), 3) for M in Ms}
+        extras["stream_launched_us_per_call"] = {
+            f"M{M}": round(stream_us_per_call(torch, lambda M=M: calls(M), S, max(2, args.steps // 4)), 3)
+            for M in Ms}
         extras["stream_read_ceiling"] = stream_read_ceiling(torch, Q, B, S * B, max(2, args.steps // 2))
     copy_calibration(torch, Q)
 
