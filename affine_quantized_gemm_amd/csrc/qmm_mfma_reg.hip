@@ -87,9 +87,10 @@ __host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
 // The tile loop is written so that no wait on a load can be forced early:
 // loaded registers are not touched in the iteration that issues them (the
 // memory counter retires in order, so an early use would also wait for every
-// later load), prefetches are unconditional (the last ones re-read the final
-// tile) and pinned ahead of the compute, and nothing on the weight side is
-// masked: positions beyond K read valid addresses and meet zero activations.
+// later load), prefetches are unconditional (past the workgroup's last tile
+// they re-read its current tile, which was just fetched) and pinned ahead of
+// the compute, and nothing on the weight side is masked: positions beyond K
+// read valid addresses and meet zero activations.
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
@@ -350,7 +351,10 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     while (tile < ntiles) {
 #pragma unroll
         for (int u = 0; u <= LA; ++u) {
-            load_tile(min(tile + LA * step, ntiles - 1), buf[(u + LA) % (LA + 1)]);
+            // past the last tile of this workgroup the prefetch re-reads the
+            // tile just loaded (cache hits) instead of another workgroup's
+            const int64_t next = tile + LA * step;
+            load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)]);
             // keep the prefetch ahead of the compute: left alone, the
             // scheduler sinks these loads past it to shorten live ranges
             __builtin_amdgcn_sched_barrier(0);
