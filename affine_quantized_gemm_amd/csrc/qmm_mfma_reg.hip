@@ -347,6 +347,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         parity ^= 1;
     };
 
+    // a workgroup with a single tile (the grid covers N) has nothing to
+    // prefetch
+    if (tile + step >= ntiles) {
+        compute_store(tile, buf[0]);
+        return;
+    }
     // buffers rotate: tile t + a*step lives in buf[(u + a) % (LA + 1)]
     while (tile < ntiles) {
 #pragma unroll
