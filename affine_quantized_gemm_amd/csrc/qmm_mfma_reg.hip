@@ -37,6 +37,8 @@
 // supplies A[l%16][8*(l/16)+e] and B[8*(l/16)+e][l%16] for e = 0..7 and
 // receives D[4*(l/16)+r][l%16], r = 0..3.  A lane thus serves row i = l%16 of
 // x and column c = l%16 of the tile, in k-slot quarter jj = l/16.
+#include <type_traits>
+
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 #include "qmm_mfma_frag.hpp"
@@ -56,10 +58,16 @@ struct ScaleRegs;
 template <int NGW, int KPW, int NP>
 struct ScaleRegs<true, NGW, KPW, NP> {
     uint32_t s[NGW], b[NGW];
+    // from a cooperative block in LDS: scales at p, biases at p + bias_off
+    __device__ __forceinline__ void from_lds(const uint8_t* p, int64_t bias_off) {
+        load_words<NGW>(reinterpret_cast<const uint16_t*>(p), s);
+        load_words<NGW>(reinterpret_cast<const uint16_t*>(p + bias_off), b);
+    }
 };
 template <int NGW, int KPW, int NP>
 struct ScaleRegs<false, NGW, KPW, NP> {
     uint32_t s[KPW][NP], b[KPW][NP];
+    __device__ __forceinline__ void from_lds(const uint8_t*, int64_t) {}  // not used by the scalar form
 };
 
 // Weight words and raw scale/bias values of one tile for one lane.
@@ -67,6 +75,7 @@ template <bool VEC, int NGW, int KPW, int NW, int NP>
 struct TileRegs {
     uint32_t w[KPW][NW];
     ScaleRegs<VEC, NGW, KPW, NP> sb;
+    uint4 sch;  // cooperative form: this lane's chunk of the tile's scale/bias block
 };
 
 // LDS of one wavefront: its activation rows for its part of K (row stride
@@ -77,6 +86,27 @@ __host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
     const int x = M * xs_row_elems(kpw, kblk) * 2;
     return x > 2048 ? x : 2048;
 }
+
+// Cooperative form of the scales and biases (multi-tile workgroups of the
+// vector form): the 16 rows x G values of a tile are one contiguous block per
+// array; the workgroup fetches it with one 16-byte chunk per lane (a few
+// lines in all, instead of one line per row per wavefront) and keeps it in
+// LDS: two tile parities x two arrays x 16 rows, row stride 2G + 16 bytes.
+__host__ __device__ inline int64_t sb_row_bytes(int64_t G) { return 2 * G + 16; }
+
+// Prefetch distance in tiles: two where the register budget allows.
+template <int DT, int BITS, int GS, int KPW, bool VEC>
+__host__ __device__ constexpr int reg_lead() {
+    return (VEC && KPW * Fmt<DT, BITS, GS>::SEG_WORDS <= 8) ? 2 : 1;
+}
+// Cooperative scale/bias blocks need a tile of lead: the chunk of tile
+// t + step, loaded with its weights an iteration earlier, is staged to LDS at
+// the end of tile t.
+template <int DT, int BITS, int GS, int KPW, bool VEC>
+__host__ __device__ constexpr bool reg_coop() {
+    return VEC && reg_lead<DT, BITS, GS, KPW, VEC>() == 2;
+}
+__host__ __device__ inline int64_t sb_lds_bytes(int64_t G) { return 4 * 16 * sb_row_bytes(G); }
 
 // W wavefronts per workgroup; wavefront w owns the KPW consecutive k-blocks
 // [w*KPW, (w+1)*KPW) of K.  One workgroup owns a tile of 16 columns at a
@@ -91,12 +121,13 @@ __host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
 // they re-read its current tile, which was just fetched) and pinned ahead of
 // the compute, and nothing on the weight side is masked: positions beyond K
 // read valid addresses and meet zero activations.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
     using F = Fmt<DT, BITS, GS>;
-    constexpr int LA = 1;
+    constexpr int LA = reg_lead<DT, BITS, GS, KPW, VEC>();
+    constexpr bool COOP = MULTI && reg_coop<DT, BITS, GS, KPW, VEC>();
     constexpr int NG = (KPW * F::KBLK + GS - 1) / GS;  // groups touched by one wavefront (vector form)
     constexpr int NGW = NG >= 2 ? NG / 2 : 1;            // 32-bit words holding NG 16-bit values
     constexpr int NU = KPW * F::PORTIONS;                // units (portions) per wavefront
@@ -131,8 +162,33 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         return (narrow || c0 + 16 <= N) ? c0 : N - 16;
     };
 
-    auto load_tile = [&](int64_t tile, Regs& r) {
+    // this lane's chunk of the cooperative block: array, row in the tile,
+    // 16-byte chunk in the row (chunks per wavefront <= 64)
+    uint8_t* const sblk = lds + static_cast<int64_t>(W) * wave_lds;
+    const int64_t sb_row = sb_row_bytes(G);
+    const int sc_cpw = COOP ? static_cast<int>(4 * G / W) : 0;
+    const bool sc_on = lane < sc_cpw;
+    const int sc_q = wave * sc_cpw + lane;
+    const int sc_arr = COOP ? sc_q / static_cast<int>(2 * G) : 0;
+    const int sc_row = COOP ? (sc_q % static_cast<int>(2 * G)) / static_cast<int>(G / 8) : 0;
+    const int sc_cc = COOP ? (sc_q % static_cast<int>(2 * G)) % static_cast<int>(G / 8) : 0;
+    const uint16_t* const sc_src = sc_arr ? biases : scales;
+    auto stage_scales = [&](uint4 chunk, int par) __attribute__((always_inline)) {
+        if (sc_on)
+            *reinterpret_cast<uint4*>(sblk + ((par * 2 + sc_arr) * 16 + sc_row) * sb_row + sc_cc * 16) = chunk;
+    };
+
+    // coop: the scale/bias chunk first (so that waiting for it does not wait
+    // for the weights), else per-lane scale/bias words after the weights
+    auto load_tile = [&](int64_t tile, Regs& r, auto coop_tag) __attribute__((always_inline)) {
+        constexpr bool coop = decltype(coop_tag)::value;
         const int64_t col0 = tile_col0(tile);
+        if constexpr (coop) {
+            if (sc_on) {
+                const int64_t srow = col0 + sc_row < N ? col0 + sc_row : N - 1;
+                r.sch = *reinterpret_cast<const uint4*>(sc_src + srow * G + sc_cc * 8);
+            }
+        }
         const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
@@ -147,7 +203,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     reinterpret_cast<const uint32_t*>(wbase + lane_row * row_bytes + code0 * BITS / 8), r.w[i]);
             }
         }
-        if constexpr (VEC) {
+        if constexpr (coop) {
+        } else if constexpr (VEC) {
             const uint16_t* sbase = scales + col0 * G;
             const uint16_t* bbase = biases + col0 * G;
             load_words<NGW>(sbase + s_off, r.sb.s);
@@ -165,210 +222,235 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         }
     };
 
-    // ---- prologue.  This wavefront's activation rows [0, M) x its part of
-    // K are read with coalesced 16-byte loads (whole lines, every lane busy)
-    // ahead of the first tile's weights, then staged through its own LDS
-    // region and read back in fragment order.  Positions >= K are zero.
-    constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
-    constexpr int XG = (16 * CPR + 63) / 64;
-    uint4 xg[XG];
-    {
-#pragma unroll
+    // MULTI: workgroups walk several tiles (prefetch, cooperative scale/bias
+    // blocks where the form allows); otherwise each owns exactly one tile
+    // (the grid covers N) and loads its scales per lane.  Separate kernels,
+    // so that each has straight-line loads and its own register allocation.
+    const int64_t step = gridDim.x;
+    auto body = [&](auto coop_tag) __attribute__((always_inline)) {
+        constexpr bool coop = decltype(coop_tag)::value;
+        // ---- prologue.  This wavefront's activation rows [0, M) x its part of
+        // K are read with coalesced 16-byte loads (whole lines, every lane busy)
+        // ahead of the first tile's weights, then staged through its own LDS
+        // region and read back in fragment order.  Positions >= K are zero.
+        constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
+        constexpr int XG = (16 * CPR + 63) / 64;
+        uint4 xg[XG];
+        {
+    #pragma unroll
+            for (int j = 0; j < XG; ++j) {
+                const int t = lane + 64 * j;
+                const int row = t / CPR, piece = t % CPR;
+                const int64_t k = kb0 * F::KBLK + piece * 8;
+                xg[j] = make_uint4(0u, 0u, 0u, 0u);
+                if (row < M && (VEC || k < K)) xg[j] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(row) * K + k);
+            }
+        }
+        Regs buf[LA + 1];
+        int64_t tile = blockIdx.x;
+        load_tile(tile, buf[0], coop_tag);
+        __builtin_amdgcn_sched_barrier(0);
+
+        uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
+    #pragma unroll
         for (int j = 0; j < XG; ++j) {
             const int t = lane + 64 * j;
             const int row = t / CPR, piece = t % CPR;
-            const int64_t k = kb0 * F::KBLK + piece * 8;
-            xg[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (row < M && (VEC || k < K)) xg[j] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(row) * K + k);
+            if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
         }
-    }
-    Regs buf[LA + 1];
-    const int64_t step = gridDim.x;
-    int64_t tile = blockIdx.x;
-    load_tile(min(tile, ntiles - 1), buf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
-#pragma unroll
-    for (int j = 0; j < XG; ++j) {
-        const int t = lane + 64 * j;
-        const int row = t / CPR, piece = t % CPR;
-        if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
-    }
-    uint4 xraw[KPW][F::STEPS];
-#pragma unroll
-    for (int i = 0; i < KPW; ++i)
-#pragma unroll
-        for (int s = 0; s < F::STEPS; ++s) {
-            const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-            xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
-            if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
-        }
-
-    Frag xa[KPW][F::STEPS];
-#pragma unroll
-    for (int i = 0; i < KPW; ++i)
-#pragma unroll
-        for (int s = 0; s < F::STEPS; ++s) xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
-
-    // Unit sums X_u = sum x and O_u = sum x*off of row c over each unit of
-    // this wavefront, on the matrix cores: with B = the activation fragment
-    // of a step (B[k][c] = x[c][k], the same register that serves as A) and
-    // A = a pattern with row u all ones and row 8 + u holding the offsets of
-    // the k-slots (u = the step's unit), one product per step accumulates
-    // D[u][c] = X_u[c] and D[8 + u][c] = O_u[c].  A lane (column c, quarter
-    // jj) receives rows 4jj..4jj+3: X_0..3, X_4..7, O_0..3, O_4..7 for
-    // jj = 0..3.  Lane (row c, quarter 0) then collects all eight of each
-    // and splits them into high and low 16-bit parts: the A operands of the
-    // unit products, whose other quarters stay zero.
-    Frag xhi, xlo, ohi, olo;
-    {
-        const int arow = lane & 15;  // A-operand row this lane supplies
-        float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int i = u / F::PORTIONS, p = u % F::PORTIONS;
-            Frag e;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t ones = DtBits<DT>::one * 0x10001u;
-                const uint32_t offs = DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v)) |
-                                      (DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v + 1)) << 16);
-                e.v[v] = arow == u ? ones : (arow == 8 + u ? offs : 0u);
+        uint4 xraw[KPW][F::STEPS];
+    #pragma unroll
+        for (int i = 0; i < KPW; ++i)
+    #pragma unroll
+            for (int s = 0; s < F::STEPS; ++s) {
+                const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
+                xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
+                if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
             }
-#pragma unroll
-            for (int st = 0; st < F::STEPS_PER_PORTION; ++st) d = mfma<DT>(e, xa[i][p * F::STEPS_PER_PORTION + st], d);
-        }
-        float xv[8], ov[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            xv[r] = d[r];
-            xv[4 + r] = __shfl(d[r], (lane & 15) + 16, 64);
-            ov[r] = __shfl(d[r], (lane & 15) + 32, 64);
-            ov[4 + r] = __shfl(d[r], (lane & 15) + 48, 64);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            uint32_t hx[2], lx[2], ho[2], lo[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int u = e + h;
-                const float vx = (u < NU && jj == 0) ? xv[u] : 0.0f;
-                const float vo = (u < NU && jj == 0) ? ov[u] : 0.0f;
-                hx[h] = DtOps<DT>::rne(vx);
-                lx[h] = DtOps<DT>::rne(vx - DtOps<DT>::to_f32(static_cast<uint16_t>(hx[h])));
-                ho[h] = DtOps<DT>::rne(vo);
-                lo[h] = DtOps<DT>::rne(vo - DtOps<DT>::to_f32(static_cast<uint16_t>(ho[h])));
-            }
-            xhi.v[e / 2] = hx[0] | (hx[1] << 16);
-            xlo.v[e / 2] = lx[0] | (lx[1] << 16);
-            ohi.v[e / 2] = ho[0] | (ho[1] << 16);
-            olo.v[e / 2] = lo[0] | (lo[1] << 16);
-        }
-    }
-    const UnpackConsts uk = unpack_consts<DT>();
 
-    // 16-bit scale or bias of unit (portion p of k-block i) of this wavefront
-    auto unit_value = [&](const Regs& r, bool want_scale, int i, int p) -> uint32_t {
-        if constexpr (VEC) {
-            const int gi = (i * F::KBLK + p * F::PC) / GS;  // compile-time after unrolling
-            const uint32_t w = want_scale ? r.sb.s[gi >> 1] : r.sb.b[gi >> 1];
-            return (w >> (16 * (gi & 1))) & 0xFFFFu;
-        } else {
-            return (want_scale ? r.sb.s[i][p] : r.sb.b[i][p]) & 0xFFFFu;
-        }
-    };
-    // B operand of the unit products: lane (column c, quarter 0) holds the
-    // values of units 0..NU-1; the other quarters are zero.
-    auto unit_frag = [&](const Regs& r, bool want_scale) -> Frag {
-        Frag f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int u0 = 2 * v, u1 = u0 + 1;
-            const uint32_t lo16 = u0 < NU ? unit_value(r, want_scale, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
-            const uint32_t hi16 = u1 < NU ? unit_value(r, want_scale, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
-            f.v[v] = jj == 0 ? (lo16 | (hi16 << 16)) : 0u;
-        }
-        return f;
-    };
+        Frag xa[KPW][F::STEPS];
+    #pragma unroll
+        for (int i = 0; i < KPW; ++i)
+    #pragma unroll
+            for (int s = 0; s < F::STEPS; ++s) xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
 
-    int parity = 0;
-    auto compute_store = [&](int64_t t, Regs& r) {
-        float4_t yacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < KPW; ++i) {
-            Frag bw[F::STEPS];
-            segment_frags<DT, BITS, GS>(r.w[i], bw, uk);
-#pragma unroll
-            for (int p = 0; p < F::PORTIONS; ++p) {
-                float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
-                    const int s = p * F::STEPS_PER_PORTION + st;
-                    acc = mfma<DT>(xa[i][s], bw[s], acc);
+        // Unit sums X_u = sum x and O_u = sum x*off of row c over each unit of
+        // this wavefront, on the matrix cores: with B = the activation fragment
+        // of a step (B[k][c] = x[c][k], the same register that serves as A) and
+        // A = a pattern with row u all ones and row 8 + u holding the offsets of
+        // the k-slots (u = the step's unit), one product per step accumulates
+        // D[u][c] = X_u[c] and D[8 + u][c] = O_u[c].  A lane (column c, quarter
+        // jj) receives rows 4jj..4jj+3: X_0..3, X_4..7, O_0..3, O_4..7 for
+        // jj = 0..3.
+        //
+        // Both unit products then fold into one matrix-core step with 32 k-slots
+        // (8 per quarter): the A operand "xo" of lane (row c, quarter q) holds
+        // units 0..7 of X_hi (q = 0), O_hi (q = 1), X_lo (q = 2), O_lo (q = 3),
+        // where hi + lo splits an fp32 sum into two 16-bit values; the matching
+        // B operand holds b_u in the even quarters and -s_u in the odd ones.
+        Frag xo;
+        {
+            const int arow = lane & 15;  // A-operand row this lane supplies
+            float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int i = u / F::PORTIONS, p = u % F::PORTIONS;
+                Frag e;
+    #pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t ones = DtBits<DT>::one * 0x10001u;
+                    const uint32_t offs = DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v)) |
+                                          (DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v + 1)) << 16);
+                    e.v[v] = arow == u ? ones : (arow == 8 + u ? offs : 0u);
                 }
-                const float sc = DtOps<DT>::to_f32(static_cast<uint16_t>(unit_value(r, true, i, p)));
-#pragma unroll
-                for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
+    #pragma unroll
+                for (int st = 0; st < F::STEPS_PER_PORTION; ++st) d = mfma<DT>(e, xa[i][p * F::STEPS_PER_PORTION + st], d);
+            }
+            const int src = (jj & 1) ? 32 : 0;  // X rows (lanes 0..31) or O rows (lanes 32..63)
+            float v8[8];
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v8[r] = __shfl(d[r], (lane & 15) + src, 64);
+                v8[4 + r] = __shfl(d[r], (lane & 15) + src + 16, 64);
+            }
+            const bool lo_part = jj >= 2;
+    #pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                uint32_t h16[2];
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int u = e + h;
+                    const float v = u < NU ? v8[u] : 0.0f;
+                    const uint32_t hi = DtOps<DT>::rne(v);
+                    const uint32_t lo = DtOps<DT>::rne(v - DtOps<DT>::to_f32(static_cast<uint16_t>(hi)));
+                    h16[h] = lo_part ? lo : hi;
+                }
+                xo.v[e / 2] = h16[0] | (h16[1] << 16);
             }
         }
-        // unit products: + sum_u b_u X_u - sum_u s_u O_u
-        const Frag bb = unit_frag(r, false);
-        yacc = mfma<DT>(xhi, bb, yacc);
-        yacc = mfma<DT>(xlo, bb, yacc);
-        if constexpr (F::HAS_OFF) {
-            Frag sn = unit_frag(r, true);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sn.v[v] ^= 0x80008000u;  // -s, exact
-            yacc = mfma<DT>(ohi, sn, yacc);
-            yacc = mfma<DT>(olo, sn, yacc);
-        }
-        // Combine the wavefronts' partial sums: every wavefront writes its
-        // partial to the buffer of this tile's parity at the start of its own
-        // LDS region (over its staged activations, which it has read by then;
-        // layout [q][lane], conflict-free); after one barrier wavefronts 0..3
-        // each sum one of the four D rows a lane holds and store it.  The
-        // next tile writes the other buffer, and the tile after that can only
-        // write this one after passing the next barrier, which the reducing
-        // wavefronts reach only after reading.
-        float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 256;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rb[q * 64 + lane] = yacc[q];
-        __syncthreads();
-        if (wave < 4) {
-            const int q = wave;
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < W; ++w) v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 256 + q * 64 + lane];
-            const int64_t col = tile_col0(t) + c;
-            const int row = 4 * jj + q;
-            if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
-        }
-        parity ^= 1;
-    };
+        const UnpackConsts uk = unpack_consts<DT>();
 
-    // a workgroup with a single tile (the grid covers N) has nothing to
-    // prefetch
-    if (tile + step >= ntiles) {
-        compute_store(tile, buf[0]);
-        return;
-    }
-    // buffers rotate: tile t + a*step lives in buf[(u + a) % (LA + 1)]
-    while (tile < ntiles) {
-#pragma unroll
-        for (int u = 0; u <= LA; ++u) {
-            // past the last tile of this workgroup the prefetch re-reads the
-            // tile just loaded (cache hits) instead of another workgroup's
-            const int64_t next = tile + LA * step;
-            load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)]);
-            // keep the prefetch ahead of the compute: left alone, the
-            // scheduler sinks these loads past it to shorten live ranges
-            __builtin_amdgcn_sched_barrier(0);
-            compute_store(tile, buf[u]);
-            tile += step;
-            if (tile >= ntiles) break;
+        // 16-bit scale or bias of unit (portion p of k-block i) of this wavefront
+        auto unit_value = [&](const Regs& r, bool want_scale, int i, int p) -> uint32_t {
+            if constexpr (VEC) {
+                const int gi = (i * F::KBLK + p * F::PC) / GS;  // compile-time after unrolling
+                const uint32_t w = want_scale ? r.sb.s[gi >> 1] : r.sb.b[gi >> 1];
+                return (w >> (16 * (gi & 1))) & 0xFFFFu;
+            } else {
+                return (want_scale ? r.sb.s[i][p] : r.sb.b[i][p]) & 0xFFFFu;
+            }
+        };
+        // B operand of the folded unit product: lane (column c, quarter q)
+        // holds b_u (q even) or -s_u (q odd) of units 0..NU-1 (zero beyond NU;
+        // -s is exact: a sign flip).
+        auto unit_frag = [&](const Regs& r) -> Frag {
+            Frag f;
+            const bool odd = (jj & 1) != 0;
+    #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int u0 = 2 * v, u1 = u0 + 1;
+                const uint32_t b0 = u0 < NU ? unit_value(r, false, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
+                const uint32_t b1 = u1 < NU ? unit_value(r, false, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
+                const uint32_t s0 = u0 < NU ? unit_value(r, true, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
+                const uint32_t s1 = u1 < NU ? unit_value(r, true, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
+                const uint32_t bias = b0 | (b1 << 16);
+                const uint32_t nscale = (s0 | (s1 << 16)) ^ 0x80008000u;
+                f.v[v] = odd ? nscale : bias;
+            }
+            return f;
+        };
+
+        int parity = 0;
+        auto compute_store = [&](int64_t t, Regs& r, uint4 next_chunk, auto coop_tag) __attribute__((always_inline)) {
+            constexpr bool coop = decltype(coop_tag)::value;
+            if constexpr (coop) {
+                // this wavefront's scales and biases of tile t, from the block in LDS
+                r.sb.from_lds(sblk + (parity * 2 * 16 + c) * sb_row + (kb0 * F::KBLK / GS) * 2, 16 * sb_row);
+            }
+            float4_t yacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+            for (int i = 0; i < KPW; ++i) {
+                Frag bw[F::STEPS];
+                segment_frags<DT, BITS, GS>(r.w[i], bw, uk);
+    #pragma unroll
+                for (int p = 0; p < F::PORTIONS; ++p) {
+                    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+                    for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
+                        const int s = p * F::STEPS_PER_PORTION + st;
+                        acc = mfma<DT>(xa[i][s], bw[s], acc);
+                    }
+                    const float sc = DtOps<DT>::to_f32(static_cast<uint16_t>(unit_value(r, true, i, p)));
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
+                }
+            }
+            // unit products: + sum_u b_u X_u - sum_u s_u O_u, one step
+            yacc = mfma<DT>(xo, unit_frag(r), yacc);
+            // the next tile's scale/bias block to the other parity; the barrier
+            // below publishes it.  That buffer was last read in the previous
+            // tile, before the previous barrier.
+            if constexpr (coop) stage_scales(next_chunk, parity ^ 1);
+            // Combine the wavefronts' partial sums: every wavefront writes its
+            // partial to the buffer of this tile's parity at the start of its own
+            // LDS region (over its staged activations, which it has read by then;
+            // layout [q][lane], conflict-free); after one barrier wavefronts 0..3
+            // each sum one of the four D rows a lane holds and store it.  The
+            // next tile writes the other buffer, and the tile after that can only
+            // write this one after passing the next barrier, which the reducing
+            // wavefronts reach only after reading.  Cooperative scale/bias blocks
+            // follow the same parity.
+            float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 256;
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) rb[q * 64 + lane] = yacc[q];
+            __syncthreads();
+            if (wave < 4) {
+                const int q = wave;
+                float v = 0.0f;
+    #pragma unroll
+                for (int w = 0; w < W; ++w) v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 256 + q * 64 + lane];
+                const int64_t col = tile_col0(t) + c;
+                const int row = 4 * jj + q;
+                if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
+            }
+            parity ^= 1;
+        };
+
+        if constexpr (!MULTI) {  // a single tile: nothing to prefetch
+            compute_store(tile, buf[0], buf[0].sch, coop_tag);
+            return;
         }
-    }
+        // the tiles after the first up to the prefetch distance (buf[0] holds
+        // the first); past the workgroup's last tile these re-read the first
+    #pragma unroll
+        for (int a = 1; a < LA; ++a) {
+            const int64_t t_a = tile + a * step;
+            load_tile(t_a < ntiles ? t_a : tile, buf[a], coop_tag);
+        }
+        // the first tile's scale/bias block, published before the tile loop
+        if constexpr (coop) {
+            stage_scales(buf[0].sch, 0);
+            __syncthreads();
+        }
+        // buffers rotate: tile t + a*step lives in buf[(u + a) % (LA + 1)]
+        while (tile < ntiles) {
+    #pragma unroll
+            for (int u = 0; u <= LA; ++u) {
+                // past the last tile of this workgroup the prefetch re-reads the
+                // tile just loaded (cache hits) instead of another workgroup's
+                const int64_t next = tile + LA * step;
+                load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)], coop_tag);
+                // keep the prefetch ahead of the compute: left alone, the
+                // scheduler sinks these loads past it to shorten live ranges
+                __builtin_amdgcn_sched_barrier(0);
+                compute_store(tile, buf[u], buf[(u + 1) % (LA + 1)].sch, coop_tag);
+                tile += step;
+                if (tile >= ntiles) break;
+            }
+        }
+    };
+    body(std::integral_constant<bool, COOP>{});
+
 }
 
 // The lane-quarter and step parts of a fragment's source position must be
@@ -416,31 +498,45 @@ inline bool pick_shape(int bits, int gs, int64_t K, RegShape& s) {
         const int64_t G = K / gs;
         const int64_t ng = (KPW * kblk + gs - 1) / gs;
         const int64_t vec_vals = ng >= 8 ? 8 : ng;  // 16-bit values per vector load
-        s = {W, KPW, W * KPW == nkb && KPW * kblk % gs == 0 && G % vec_vals == 0 && ng % 2 == 0};
+        s = {W, KPW, W * KPW == nkb && KPW * kblk % gs == 0 && G % vec_vals == 0 && ng % 2 == 0 && G % 8 == 0 &&
+                         4 * G <= 64 * W};
         return true;
     }
     return false;
 }
 
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
-hipError_t launch_shape(const MatmulArgs& a) {
-    const int64_t ntiles = (a.N + 15) / 16;
-    const size_t lds = static_cast<size_t>(W) * wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK);
-    // workgroups resident at once on 256 CUs (16 wavefronts per CU); each walks several tiles
+// workgroups resident at once on 256 CUs (16 wavefronts per CU); each walks
+// ntiles / grid tiles
+inline int64_t reg_grid(int64_t ntiles, int W) {
     const int64_t resident = 256 * (16 / W);
-    const int64_t grid = ntiles < resident ? ntiles : resident;
+    return ntiles < resident ? ntiles : resident;
+}
+
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI>
+hipError_t launch_shape_m(const MatmulArgs& a) {
+    const int64_t ntiles = (a.N + 15) / 16;
+    const int64_t grid = reg_grid(ntiles, W);
+    const size_t lds = static_cast<size_t>(W) * wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK) +
+                       (MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(a.K / GS)) : 0);
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC>),
+            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC>), dim3(static_cast<unsigned>(grid)), dim3(64 * W),
-                       lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
-                       static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
-                       a.K);
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * W), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
+                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
+                       static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
     return hipGetLastError();
+}
+
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
+hipError_t launch_shape(const MatmulArgs& a) {
+    const int64_t ntiles = (a.N + 15) / 16;
+    if (ntiles > reg_grid(ntiles, W)) return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true>(a);
+    return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false>(a);
 }
 
 template <int DT, int BITS, int GS>
