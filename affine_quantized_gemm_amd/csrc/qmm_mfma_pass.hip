@@ -23,8 +23,8 @@
 // fp16/bf16 values q + off, and per unit u (a run of K inside one group)
 //   y += s_u * P_u + b_u * X_u - s_u * O_u,
 // P_u on the matrix cores, X_u = sum x and O_u = sum x*off from the
-// activation block (also on the matrix cores), the last two terms as small
-// products with hi/lo-split operands.
+// activation block (also on the matrix cores), the last two terms as one
+// small matrix step with hi/lo-split operands.
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 #include "qmm_mfma_frag.hpp"
@@ -57,7 +57,10 @@ struct PassRegs {
     uint32_t s[F::PORTIONS], b[F::PORTIONS];
 };
 
-template <int DT, int BITS, int GS>
+// SV: K is a whole number of k-blocks and a row's group count is a multiple
+// of the units per k-block, so a k-block's scales (and biases) are read with
+// one aligned 4- or 8-byte load per lane instead of one per unit.
+template <int DT, int BITS, int GS, bool SV>
 __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
@@ -123,12 +126,26 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
         code0 = code0 < K ? code0 : K - F::SEG;
         const uint8_t* wrow = reinterpret_cast<const uint8_t*>(wq) + (col0 + lane_row) * row_bytes;
         load_segment<BITS, F::SEG_WORDS>(reinterpret_cast<const uint32_t*>(wrow + code0 * BITS / 8), r.w);
+        if constexpr (SV && F::PORTIONS == 2) {
+            const int64_t at = (col0 + lane_row) * G + kbc * 2;
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(scales + at);
+            const uint32_t bw = *reinterpret_cast<const uint32_t*>(biases + at);
+            r.s[0] = sw; r.s[1] = sw >> 16;
+            r.b[0] = bw; r.b[1] = bw >> 16;
+        } else if constexpr (SV && F::PORTIONS == 4) {
+            const int64_t at = (col0 + lane_row) * G + kbc * 4;
+            const uint2 sw = *reinterpret_cast<const uint2*>(scales + at);
+            const uint2 bw = *reinterpret_cast<const uint2*>(biases + at);
+            r.s[0] = sw.x; r.s[1] = sw.x >> 16; r.s[2] = sw.y; r.s[3] = sw.y >> 16;
+            r.b[0] = bw.x; r.b[1] = bw.x >> 16; r.b[2] = bw.y; r.b[3] = bw.y >> 16;
+        } else {
 #pragma unroll
-        for (int p = 0; p < F::PORTIONS; ++p) {
-            int64_t g = (kbc * F::KBLK + static_cast<int64_t>(p) * F::PC) / GS;
-            g = g < G ? g : G - 1;
-            r.s[p] = scales[(col0 + lane_row) * G + g];
-            r.b[p] = biases[(col0 + lane_row) * G + g];
+            for (int p = 0; p < F::PORTIONS; ++p) {
+                int64_t g = (kbc * F::KBLK + static_cast<int64_t>(p) * F::PC) / GS;
+                g = g < G ? g : G - 1;
+                r.s[p] = scales[(col0 + lane_row) * G + g];
+                r.b[p] = biases[(col0 + lane_row) * G + g];
+            }
         }
     };
     // the activation block of the loads just issued -> this wavefront's LDS
@@ -145,14 +162,17 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     const UnpackConsts uk = unpack_consts<DT>();
     const int arow = lane & 15;
 
-    auto unit_frag = [&](const uint32_t (&v)[F::PORTIONS]) -> Frag {
+    auto unit_frag = [&](const Regs& r) -> Frag {
         Frag f;
+        const bool odd = (jj & 1) != 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int u0 = 2 * q, u1 = u0 + 1;
-            const uint32_t lo16 = u0 < NU ? (v[u0 < NU ? u0 : 0] & 0xFFFFu) : 0u;
-            const uint32_t hi16 = u1 < NU ? (v[u1 < NU ? u1 : 0] & 0xFFFFu) : 0u;
-            f.v[q] = jj == 0 ? (lo16 | (hi16 << 16)) : 0u;
+            const uint32_t b0 = u0 < NU ? (r.b[u0 < NU ? u0 : 0] & 0xFFFFu) : 0u;
+            const uint32_t b1 = u1 < NU ? (r.b[u1 < NU ? u1 : 0] & 0xFFFFu) : 0u;
+            const uint32_t s0 = u0 < NU ? (r.s[u0 < NU ? u0 : 0] & 0xFFFFu) : 0u;
+            const uint32_t s1 = u1 < NU ? (r.s[u1 < NU ? u1 : 0] & 0xFFFFu) : 0u;
+            f.v[q] = odd ? ((s0 | (s1 << 16)) ^ 0x80008000u) : (b0 | (b1 << 16));
         }
         return f;
     };
@@ -171,8 +191,9 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
             xa[s] = x_frag<BITS, DT>(*reinterpret_cast<const uint4*>(xs + c * PF::XS_ROW + kk));
         }
         // unit sums X_u, O_u of this block on the matrix cores (rows u and
-        // 8 + u of D), collected by lane (row c, quarter 0) and split hi/lo
-        Frag xhi, xlo, ohi, olo;
+        // 8 + u of D), folded into one A operand "xo": lane (row c, quarter
+        // q) holds units 0..3 of X_hi (q = 0), O_hi (1), X_lo (2), O_lo (3)
+        Frag xo;
         {
             float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -189,46 +210,30 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
                 for (int st = 0; st < F::STEPS_PER_PORTION; ++st)
                     d = mfma<DT>(e, xa[u * F::STEPS_PER_PORTION + st], d);
             }
-            float xv[4], ov[4];
+            // X_0..3 arrive in quarter 0, O_0..3 in quarter 2 (NU <= 4)
+            const int src = (jj & 1) ? 32 : 0;
+            float v4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xv[q] = d[q];
-                ov[q] = __shfl(d[q], (lane & 15) + 32, 64);
-            }
+            for (int q = 0; q < 4; ++q) v4[q] = __shfl(d[q], (lane & 15) + src, 64);
+            const bool lo_part = jj >= 2;
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
-                uint32_t hx[2], lx[2], ho[2], lo[2];
+                uint32_t h16[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int u = e + h;
-                    const float vx = (u < NU && jj == 0) ? xv[u] : 0.0f;
-                    const float vo = (u < NU && jj == 0) ? ov[u] : 0.0f;
-                    hx[h] = DtOps<DT>::rne(vx);
-                    lx[h] = DtOps<DT>::rne(vx - DtOps<DT>::to_f32(static_cast<uint16_t>(hx[h])));
-                    ho[h] = DtOps<DT>::rne(vo);
-                    lo[h] = DtOps<DT>::rne(vo - DtOps<DT>::to_f32(static_cast<uint16_t>(ho[h])));
+                    const float v = u < NU ? v4[u] : 0.0f;
+                    const uint32_t hi = DtOps<DT>::rne(v);
+                    const uint32_t lo = DtOps<DT>::rne(v - DtOps<DT>::to_f32(static_cast<uint16_t>(hi)));
+                    h16[h] = lo_part ? lo : hi;
                 }
-                xhi.v[e / 2] = hx[0] | (hx[1] << 16);
-                xlo.v[e / 2] = lx[0] | (lx[1] << 16);
-                ohi.v[e / 2] = ho[0] | (ho[1] << 16);
-                olo.v[e / 2] = lo[0] | (lo[1] << 16);
+                xo.v[e / 2] = h16[0] | (h16[1] << 16);
             }
-            xhi.v[2] = xhi.v[3] = xlo.v[2] = xlo.v[3] = 0u;
-            ohi.v[2] = ohi.v[3] = olo.v[2] = olo.v[3] = 0u;
+            xo.v[2] = xo.v[3] = 0u;
         }
-        // unit products first (their operands die here): + b.X - s.O
-        {
-            const Frag bb = unit_frag(r.b);
-            yacc = mfma<DT>(xhi, bb, yacc);
-            yacc = mfma<DT>(xlo, bb, yacc);
-            if constexpr (F::HAS_OFF) {
-                Frag sn = unit_frag(r.s);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) sn.v[v] ^= 0x80008000u;  // -s, exact
-                yacc = mfma<DT>(ohi, sn, yacc);
-                yacc = mfma<DT>(olo, sn, yacc);
-            }
-        }
+        // unit products first (their operand dies here): + b.X - s.O in one
+        // matrix step (B: b_u in even quarters, -s_u in odd ones)
+        yacc = mfma<DT>(xo, unit_frag(r), yacc);
         // weights
         uint32_t wcopy[F::SEG_WORDS];
 #pragma unroll
@@ -289,8 +294,8 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     }
 }
 
-template <int DT, int BITS, int GS>
-hipError_t launch_pass_t(const MatmulArgs& a) {
+template <int DT, int BITS, int GS, bool SV>
+hipError_t launch_pass_sv(const MatmulArgs& a) {
     using PF = PassFmt<DT, BITS, GS>;
     const int64_t ntiles = (a.N + 15) / 16;
     const int64_t gx = ntiles < 256 ? ntiles : 256;
@@ -298,15 +303,23 @@ hipError_t launch_pass_t(const MatmulArgs& a) {
     const size_t lds = static_cast<size_t>(PF::LDS_BYTES);
     if (lds > 65536) {
         static const hipError_t attr =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_pass_kernel<DT, BITS, GS>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_pass_kernel<DT, BITS, GS, SV>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((mfma_pass_kernel<DT, BITS, GS>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+    hipLaunchKernelGGL((mfma_pass_kernel<DT, BITS, GS, SV>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
                        dim3(64 * PW), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
                        static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
                        static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
     return hipGetLastError();
+}
+
+template <int DT, int BITS, int GS>
+hipError_t launch_pass_t(const MatmulArgs& a) {
+    using F = Fmt<DT, BITS, GS>;
+    const int64_t G = a.K / GS;
+    const bool sv = F::PORTIONS > 1 && a.K % F::KBLK == 0 && G % F::PORTIONS == 0;
+    return sv ? launch_pass_sv<DT, BITS, GS, true>(a) : launch_pass_sv<DT, BITS, GS, false>(a);
 }
 
 }  // namespace

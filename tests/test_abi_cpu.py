@@ -147,20 +147,14 @@ def test_probe_validation():
 
 def test_dispatch_follows_measured_crossovers():
     """qmm_select_kernel encodes the crossovers measured on MI355X
-    (affine_quantized_gemm_amd/sweep.py): VALU only at M <= 2 where the
-    register-resident MFMA kernel cannot run or for 8-bit codes on shapes up
-    to 4096 x 4096; the register-resident kernel wherever it runs; the pass
-    kernel elsewhere."""
+    (affine_quantized_gemm_amd/sweep.py): the register-resident MFMA kernel
+    wherever it runs (M <= 16, K <= 4096), the pass kernel everywhere else."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
     sel = lambda dt, b, gs, M, N, K: Q.kernel_name(Q.select_kernel(dt, b, gs, M, N, K))
-    for M in (1, 2):
-        assert sel(f16, 4, 64, M, 4096, 14336) == "valu_splitfree"
-        assert sel(f16, 8, 64, M, 4096, 4096) == "valu_splitfree"
+    for M in (1, 2, 3, 4, 6, 8, 16):
         assert sel(f16, 4, 64, M, 4096, 4096) == "mfma_splitfree_reg"
-        assert sel(bf16, 8, 64, M, 151936, 4096) == "mfma_splitfree_reg"
-    for M in (3, 4, 6, 8, 16):
-        assert sel(f16, 4, 64, M, 4096, 4096) == "mfma_splitfree_reg"
+        assert sel(f16, 8, 64, M, 4096, 4096) == "mfma_splitfree_reg"
         assert sel(bf16, 4, 64, M, 151936, 4096) == "mfma_splitfree_reg"
         assert sel(f16, 4, 64, M, 4096, 14336) == "mfma_splitfree_pass"
     for M in (17, 24, 32, 36, 48, 64):
