@@ -6,11 +6,13 @@ K = N = 4096 (a q/o-projection shape), 4-bit codes, group size 64, fp16
 activations ~N(0, 1), weights ~N(0, 0.02).  A stack of distinct quantized
 matrices, more than twice the 256 MiB Infinity Cache, is cycled call by call
 so the weights stream from HBM.  One step = one call per matrix of the stack
-at M = 4, then one per matrix at M = 6, issued by replaying a HIP graph
-captured from those calls (one graph per M; the launches cost more host time
-than a verify-shape kernel runs, so issuing them one by one from Python would
-time the host).  The one-by-one rate is reported beside it.  Other workloads
-(``--workload``) are the batched-decode shapes and the wide LM head.
+at M = 4, then one per matrix at M = 6 (several passes over a stack of fewer
+than 32 matrices, so that every replayed graph holds at least 32 calls),
+issued by replaying a HIP graph captured from those calls (one graph per M;
+the launches cost more host time than a verify-shape kernel runs, so issuing
+them one by one from Python would time the host).  The one-by-one rate is
+reported beside it.  Other workloads (``--workload``) are the batched-decode
+shapes and the wide LM head.
 
 Metric: effective weight GB/s = (packed weight bytes + 4 bytes of scale and
 bias per group) / time per call, GB = 1e9 bytes -- the byte count of the
@@ -255,11 +257,13 @@ def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
     pool.fill_(1)
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     views = [pool[i * B16:(i + 1) * B16] for i in range(n)]
+    passes = max(1, -(-32 // n))  # at least 32 launches per replayed graph
     best = None
     for grid in (1024, 2048, 4096):
         def reads(grid=grid):
-            for v in views:
-                Q.probe_stream_read(v, sink, grid)
+            for _ in range(passes):
+                for v in views:
+                    Q.probe_stream_read(v, sink, grid)
         g = capture(torch, reads)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -267,7 +271,7 @@ def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n * passes)
         if best is None or us < best[0]:
             best = (us, grid)
     del pool
@@ -317,10 +321,15 @@ def main():
     ys = {M: torch.empty((M, N), dtype=tdt, device=dev) for M in Ms}
     torch.cuda.synchronize()
 
+    # passes over the stack per step and M: at least 32 calls per replayed
+    # graph, so that a graph launch is not charged to a handful of calls
+    P = max(1, -(-32 // S))
+
     def calls(M):
         x, y = xs[M], ys[M]
-        for (wq, sc, bi) in stack:
-            Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
+        for _ in range(P):
+            for (wq, sc, bi) in stack:
+                Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
 
     # The step's launches are captured once per M into a HIP graph and the
     # graphs are replayed: the calls are launch-bound from Python (a few us
@@ -349,8 +358,8 @@ def main():
     wall = time.perf_counter() - t0
     ms = e_start.elapsed_time(e_end)
     per_m = {M: sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) * 1e3
-             / (args.steps * S) for j, M in enumerate(Ms)}
-    ncalls = args.steps * S * len(Ms)
+             / (args.steps * S * P) for j, M in enumerate(Ms)}
+    ncalls = args.steps * S * P * len(Ms)
     gbs = B * ncalls / (ms * 1e-3) / 1e9
 
     # ---- roofline of the matmul kernel: algorithmic bytes / mean launch duration
@@ -366,7 +375,7 @@ def main():
     extras = {}
     if not args.no_extras:
         extras["stream_launched_us_per_call"] = {
-            f"M{M}": round(stream_us_per_call(torch, lambda M=M: calls(M), S, max(2, args.steps // 4)), 3)
+            f"M{M}": round(stream_us_per_call(torch, lambda M=M: calls(M), S * P, max(2, args.steps // 4)), 3)
             for M in Ms}
         extras["stream_read_ceiling"] = stream_read_ceiling(torch, Q, B, S * B, max(2, args.steps // 2))
     copy_calibration(torch, Q)
@@ -386,9 +395,10 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: M in {list(Ms)}, K={K}, N={N}, {bits}-bit, group {gs}, {dt}; "
-                               f"{S} distinct matrices ({S * B / 2**20:.0f} MiB) cycled per call",
+                               f"{S} distinct matrices ({S * B / 2**20:.0f} MiB) cycled per call, "
+                               f"{P} pass(es) over them per M per step",
                    "workload_name": args.workload,
-                   "M": list(Ms), "N": N, "K": K, "bits": bits, "group_size": gs, "stack": S,
+                   "M": list(Ms), "N": N, "K": K, "bits": bits, "group_size": gs, "stack": S, "passes": P,
                    "kernel": kernels},
         "us_per_call": {f"M{M}": round(per_m[M], 3) for M in Ms},
         "weight_gbs_per_m": {f"M{M}": round(B / (per_m[M] * 1e-6) / 1e9, 1) for M in Ms},
