@@ -297,9 +297,17 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
 template <int DT, int BITS, int GS, bool SV>
 hipError_t launch_pass_sv(const MatmulArgs& a) {
     using PF = PassFmt<DT, BITS, GS>;
+    // For 2 or 4 row blocks, one resident workgroup per CU in all: the gy
+    // 16-row blocks of a column slot run at the same time and walk the same
+    // tiles, and (256 / gy being a multiple of 8, the XCD count) their linear
+    // ids fall on the same XCD, so a tile's weights come from HBM once and
+    // from that XCD's L2 for the other blocks.  For 3 blocks the slot counts
+    // that keep that alignment split the tiles unevenly or idle a quarter of
+    // the CUs (measured slower), so each row block walks the tiles on its own.
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t gx = ntiles < 256 ? ntiles : 256;
     const int gy = static_cast<int>((a.M + 15) / 16);
+    const int64_t slots = (gy == 2 || gy == 4) ? 256 / gy : 256;
+    const int64_t gx = ntiles < slots ? ntiles : slots;
     const size_t lds = static_cast<size_t>(PF::LDS_BYTES);
     if (lds > 65536) {
         static const hipError_t attr =
