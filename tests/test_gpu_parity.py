@@ -205,3 +205,17 @@ def test_pass_kernel_multipass(Q, K, dt, bits, gs):
         print(f"pass {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
         ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=K + M + bits, kernel=Q.KERNEL_MFMA_PASS)
         assert ok, (M, N, worst)
+
+
+@pytest.mark.parametrize("dt,bits,gs", COMBOS)
+def test_multi_tile_ragged(Q, dt, bits, gs):
+    """More column tiles than resident workgroups (258 tiles of 16 over 256
+    workgroups) with a ragged last tile: the persistent multi-tile kernel,
+    its prefetch past a workgroup's last tile, and (vector form) the
+    cooperative scale/bias blocks, for every format."""
+    M, N, K = 6, 16 * 257 + 5, 4096
+    print(f"multi {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
+    ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=bits * 100 + gs, kernel=Q.KERNEL_MFMA_REG, outlier=0.01)
+    assert ok, worst
+    ok, worst = run_case(Q, dt, bits, gs, 16, N, K, seed=bits * 100 + gs + 1, kernel=Q.KERNEL_MFMA_REG)
+    assert ok, worst
