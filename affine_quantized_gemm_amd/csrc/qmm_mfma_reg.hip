@@ -99,12 +99,13 @@ template <int DT, int BITS, int GS, int KPW, bool VEC>
 __host__ __device__ constexpr int reg_lead() {
     return (VEC && KPW * Fmt<DT, BITS, GS>::SEG_WORDS <= 8) ? 2 : 1;
 }
-// Cooperative scale/bias blocks need a tile of lead: the chunk of tile
-// t + step, loaded with its weights an iteration earlier, is staged to LDS at
-// the end of tile t.
+// Cooperative scale/bias blocks (vector form) need a tile of lead: the chunk
+// of tile t + step is staged to LDS at the end of tile t, so it is loaded an
+// iteration earlier -- with that tile's weights at prefetch distance 2, in a
+// ring of its own two tiles ahead at distance 1.
 template <int DT, int BITS, int GS, int KPW, bool VEC>
 __host__ __device__ constexpr bool reg_coop() {
-    return VEC && reg_lead<DT, BITS, GS, KPW, VEC>() == 2;
+    return VEC;
 }
 __host__ __device__ inline int64_t sb_lds_bytes(int64_t G) { return 4 * 16 * sb_row_bytes(G); }
 
@@ -180,15 +181,17 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
 
     // coop: the scale/bias chunk first (so that waiting for it does not wait
     // for the weights), else per-lane scale/bias words after the weights
+    auto load_chunk = [&](int64_t tile, uint4& dst) __attribute__((always_inline)) {
+        if (sc_on) {
+            const int64_t col0 = tile_col0(tile);
+            const int64_t srow = col0 + sc_row < N ? col0 + sc_row : N - 1;
+            dst = *reinterpret_cast<const uint4*>(sc_src + srow * G + sc_cc * 8);
+        }
+    };
     auto load_tile = [&](int64_t tile, Regs& r, auto coop_tag) __attribute__((always_inline)) {
         constexpr bool coop = decltype(coop_tag)::value;
         const int64_t col0 = tile_col0(tile);
-        if constexpr (coop) {
-            if (sc_on) {
-                const int64_t srow = col0 + sc_row < N ? col0 + sc_row : N - 1;
-                r.sch = *reinterpret_cast<const uint4*>(sc_src + srow * G + sc_cc * 8);
-            }
-        }
+        if constexpr (coop && LA == 2) load_chunk(tile, r.sch);
         const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
@@ -427,9 +430,15 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             const int64_t t_a = tile + a * step;
             load_tile(t_a < ntiles ? t_a : tile, buf[a], coop_tag);
         }
+        // distance 1: the chunks of the first two tiles (then two ahead)
+        uint4 sch2[2];
+        if constexpr (coop && LA == 1) {
+            load_chunk(tile, sch2[0]);
+            load_chunk(tile + step < ntiles ? tile + step : tile, sch2[1]);
+        }
         // the first tile's scale/bias block, published before the tile loop
         if constexpr (coop) {
-            stage_scales(buf[0].sch, 0);
+            stage_scales(LA == 2 ? buf[0].sch : sch2[0], 0);
             __syncthreads();
         }
         // buffers rotate: tile t + a*step lives in buf[(u + a) % (LA + 1)]
@@ -439,11 +448,16 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 // past the last tile of this workgroup the prefetch re-reads the
                 // tile just loaded (cache hits) instead of another workgroup's
                 const int64_t next = tile + LA * step;
+                if constexpr (coop && LA == 1) {
+                    // slot u held this tile's chunk, staged an iteration ago
+                    const int64_t next2 = tile + 2 * step;
+                    load_chunk(next2 < ntiles ? next2 : tile, sch2[u]);
+                }
                 load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)], coop_tag);
                 // keep the prefetch ahead of the compute: left alone, the
                 // scheduler sinks these loads past it to shorten live ranges
                 __builtin_amdgcn_sched_barrier(0);
-                compute_store(tile, buf[u], buf[(u + 1) % (LA + 1)].sch, coop_tag);
+                compute_store(tile, buf[u], LA == 2 ? buf[(u + 1) % (LA + 1)].sch : sch2[(u + 1) % 2], coop_tag);
                 tile += step;
                 if (tile >= ntiles) break;
             }
