@@ -143,13 +143,15 @@ __device__ __forceinline__ UnpackConsts unpack_consts() {
 // 4-bit: one word (8 codes) -> q + off in order 0,4,1,5,2,6,3,7.  fp16 takes
 // the odd nibbles in place (64 + q, via magic4), bf16 shifts them down
 // (its 7 mantissa bits cannot hold a code at bits 4..7).
-template <int DT>
+// UNI: every code carries the same offset (fp16 shifts the odd nibbles
+// down too, two more operations per word).
+template <int DT, bool UNI = false>
 __device__ __forceinline__ Frag unpack4(uint32_t w, const UnpackConsts& k) {
     Frag f;
     const uint32_t w8 = w >> 8;
     f.v[0] = and_or(w, k.nib, k.magic);
     f.v[2] = and_or(w8, k.nib, k.magic);
-    if constexpr (DT == DT_F16) {
+    if constexpr (DT == DT_F16 && !UNI) {
         f.v[1] = and_or(w, k.nib_hi, k.magic4);
         f.v[3] = and_or(w8, k.nib_hi, k.magic4);
     } else {
@@ -194,7 +196,7 @@ __device__ __forceinline__ Frag unpack8(uint32_t w0, uint32_t w1) {
 }
 
 // Segment words -> STEPS weight fragments, with the lane swaps applied.
-template <int DT, int BITS, int GS, int NW, int NS>
+template <int DT, int BITS, int GS, int NW, int NS, bool UNI = false>
 __device__ __forceinline__ void segment_frags(uint32_t (&w)[NW], Frag (&b)[NS], const UnpackConsts& k) {
     static_assert(NW == Fmt<DT, BITS, GS>::SEG_WORDS && NS == Fmt<DT, BITS, GS>::STEPS, "segment shape");
     if constexpr (BITS == 4) {
@@ -207,7 +209,7 @@ __device__ __forceinline__ void segment_frags(uint32_t (&w)[NW], Frag (&b)[NS], 
             swap16(w[2], w[3]);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = unpack4<DT>(w[s], k);
+        for (int s = 0; s < 4; ++s) b[s] = unpack4<DT, UNI>(w[s], k);
     } else if constexpr (BITS == 8) {
         if constexpr (GS == 32) {
             swap32(w[0], w[2]);

@@ -19,12 +19,12 @@
 // read with coalesced 16-byte loads, staged through the wavefront's own LDS
 // region and read back in fragment order.
 //
-// Arithmetic as in the register-resident kernel: codes become exact
-// fp16/bf16 values q + off, and per unit u (a run of K inside one group)
-//   y += s_u * P_u + b_u * X_u - s_u * O_u,
-// P_u on the matrix cores, X_u = sum x and O_u = sum x*off from the
-// activation block (also on the matrix cores), the last two terms as one
-// small matrix step with hi/lo-split operands.
+// Arithmetic: codes become exact fp16/bf16 values q + off with one offset
+// for every code, and per unit u (a run of K inside one group)
+//   y += s_u * P_u + (b_u - off * s_u) * X_u,
+// P_u = sum x * (q + off) and X_u = sum x on the matrix cores (the block
+// changes every iteration, so the unit sums are recomputed each time and
+// kept as cheap as possible: two per-lane FMAs per output and unit).
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 #include "qmm_mfma_frag.hpp"
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     using F = Fmt<DT, BITS, GS>;
     using PF = PassFmt<DT, BITS, GS>;
     using Regs = PassRegs<DT, BITS, GS>;
-    constexpr int NU = PF::NU;
+    // the code offset shared by every code (uniform unpack)
+    constexpr float UOFF = F::off(0);
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
@@ -101,14 +102,12 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
         return (narrow || c0 + 16 <= N) ? c0 : N - 16;
     };
 
-    // Loads of iteration `it` = (tile it / P, pass it % P): the activation
+    // Loads of iteration (tile, pass): the activation
     // block first (into xg), then the weight segment, scales and biases.  A
     // wavefront whose k-block lies beyond K in the last pass reads valid
     // addresses and gets a zero activation block, so it adds exact zeros.
     uint4 xg[PF::XG];
-    auto load_it = [&](int64_t it, Regs& r) {
-        const int64_t tile = static_cast<int64_t>(blockIdx.x) + (it / P) * gridDim.x;
-        const int pass = static_cast<int>(it % P);
+    auto load_it = [&](int64_t tile, int pass, Regs& r) {
         const int64_t col0 = tile_col0(tile);
         const int64_t kb = static_cast<int64_t>(pass) * PW + wave;
         const bool kvalid = kb < nkb;
@@ -160,28 +159,12 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     };
 
     const UnpackConsts uk = unpack_consts<DT>();
-    const int arow = lane & 15;
 
-    auto unit_frag = [&](const Regs& r) -> Frag {
-        Frag f;
-        const bool odd = (jj & 1) != 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int u0 = 2 * q, u1 = u0 + 1;
-            const uint32_t b0 = u0 < NU ? (r.b[u0 < NU ? u0 : 0] & 0xFFFFu) : 0u;
-            const uint32_t b1 = u1 < NU ? (r.b[u1 < NU ? u1 : 0] & 0xFFFFu) : 0u;
-            const uint32_t s0 = u0 < NU ? (r.s[u0 < NU ? u0 : 0] & 0xFFFFu) : 0u;
-            const uint32_t s1 = u1 < NU ? (r.s[u1 < NU ? u1 : 0] & 0xFFFFu) : 0u;
-            f.v[q] = odd ? ((s0 | (s1 << 16)) ^ 0x80008000u) : (b0 | (b1 << 16));
-        }
-        return f;
-    };
 
     float4_t yacc = {0.0f, 0.0f, 0.0f, 0.0f};
     int parity = 0;
 
-    auto process = [&](int64_t it, const Regs& r) {
-        const int pass = static_cast<int>(it % P);
+    auto process = [&](int64_t tile, int pass, const Regs& r) {
         // this iteration's activation block, staged at the top of the
         // iteration, in fragment order
         Frag xa[F::STEPS];
@@ -190,67 +173,39 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
             const int kk = F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
             xa[s] = x_frag<BITS, DT>(*reinterpret_cast<const uint4*>(xs + c * PF::XS_ROW + kk));
         }
-        // unit sums X_u, O_u of this block on the matrix cores (rows u and
-        // 8 + u of D), folded into one A operand "xo": lane (row c, quarter
-        // q) holds units 0..3 of X_hi (q = 0), O_hi (1), X_lo (2), O_lo (3)
-        Frag xo;
-        {
-            float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                Frag e;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint32_t ones = DtBits<DT>::one * 0x10001u;
-                    const uint32_t offs = DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v)) |
-                                          (DtBits<DT>::of(slot_off<DT, BITS, GS>(2 * v + 1)) << 16);
-                    e.v[v] = arow == u ? ones : (arow == 8 + u ? offs : 0u);
-                }
-#pragma unroll
-                for (int st = 0; st < F::STEPS_PER_PORTION; ++st)
-                    d = mfma<DT>(e, xa[u * F::STEPS_PER_PORTION + st], d);
-            }
-            // X_0..3 arrive in quarter 0, O_0..3 in quarter 2 (NU <= 4)
-            const int src = (jj & 1) ? 32 : 0;
-            float v4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v4[q] = __shfl(d[q], (lane & 15) + src, 64);
-            const bool lo_part = jj >= 2;
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                uint32_t h16[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int u = e + h;
-                    const float v = u < NU ? v4[u] : 0.0f;
-                    const uint32_t hi = DtOps<DT>::rne(v);
-                    const uint32_t lo = DtOps<DT>::rne(v - DtOps<DT>::to_f32(static_cast<uint16_t>(hi)));
-                    h16[h] = lo_part ? lo : hi;
-                }
-                xo.v[e / 2] = h16[0] | (h16[1] << 16);
-            }
-            xo.v[2] = xo.v[3] = 0u;
-        }
-        // unit products first (their operand dies here): + b.X - s.O in one
-        // matrix step (B: b_u in even quarters, -s_u in odd ones)
-        yacc = mfma<DT>(xo, unit_frag(r), yacc);
-        // weights
+        // Every code carries the same offset UOFF here (fp16 4-bit codes
+        // take their odd nibbles shifted down as well), so O_u = UOFF * X_u
+        // and per unit u
+        //   y += s_u * P_u + (b_u - UOFF * s_u) * X_u,
+        // with P_u = sum x * (q + UOFF) and X_u = sum x both on the matrix
+        // cores: X_u as the product with an all-ones B operand, which lands
+        // in the accumulator layout directly (row sums repeated across the
+        // columns), so both terms are per-lane FMAs.
         uint32_t wcopy[F::SEG_WORDS];
 #pragma unroll
         for (int q = 0; q < F::SEG_WORDS; ++q) wcopy[q] = r.w[q];
         Frag bw[F::STEPS];
-        segment_frags<DT, BITS, GS>(wcopy, bw, uk);
+        segment_frags<DT, BITS, GS, F::SEG_WORDS, F::STEPS, true>(wcopy, bw, uk);
+        Frag ones;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ones.v[v] = DtBits<DT>::one * 0x10001u;
 #pragma unroll
         for (int p = 0; p < F::PORTIONS; ++p) {
             float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            float4_t xs4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int st = 0; st < F::STEPS_PER_PORTION; ++st) {
                 const int s = p * F::STEPS_PER_PORTION + st;
                 acc = mfma<DT>(xa[s], bw[s], acc);
+                xs4 = mfma<DT>(xa[s], ones, xs4);
             }
             const float sc = DtOps<DT>::to_f32(static_cast<uint16_t>(r.s[p]));
+            const float bp = __fmaf_rn(-UOFF, sc, DtOps<DT>::to_f32(static_cast<uint16_t>(r.b[p])));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
+            for (int q = 0; q < 4; ++q) {
+                yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
+                yacc[q] = __fmaf_rn(bp, xs4[q], yacc[q]);
+            }
         }
         if (pass == P - 1) {
             // combine the wavefronts' partial tiles (parity double buffer,
@@ -264,7 +219,6 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
                 float v = 0.0f;
 #pragma unroll
                 for (int w = 0; w < PW; ++w) v += rb[(w * 4 + q) * 64 + lane];
-                const int64_t tile = static_cast<int64_t>(blockIdx.x) + (it / P) * gridDim.x;
                 const int64_t col = tile_col0(tile) + c;
                 const int row = 4 * jj + q;
                 if (col < N && row < Mloc) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
@@ -279,17 +233,32 @@ __global__ __launch_bounds__(64 * PW, 4) void mfma_pass_kernel(
     // wait for them) goes to LDS, replacing the previous block, whose
     // fragments this wavefront has already read (its LDS accesses execute in
     // order); then the next iteration's loads are issued, then cur computes.
+    // (tile, pass) of the current and of the next iteration, advanced
+    // without divisions; past the last iteration the prefetch re-reads the
+    // last one
     Regs buf[2];
-    load_it(0, buf[0]);
+    const int64_t tstep = gridDim.x;
+    int64_t tile = blockIdx.x;
+    int pass = 0;
+    int64_t ntile = tile;
+    int npass = 0;
+    auto advance = [&](int64_t& t, int& p) {
+        if (++p == P) {
+            p = 0;
+            t += tstep;
+        }
+    };
+    load_it(tile, 0, buf[0]);
     for (int64_t it = 0; it < n_it; it += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t cur = it + u;
-            if (cur >= n_it) break;
+            if (it + u >= n_it) break;
             stage_x();
-            load_it(cur + 1 < n_it ? cur + 1 : n_it - 1, buf[u ^ 1]);
+            if (it + u + 1 < n_it) advance(ntile, npass);
+            load_it(ntile, npass, buf[u ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
-            process(cur, buf[u]);
+            process(tile, pass, buf[u]);
+            advance(tile, pass);
         }
     }
 }
