@@ -135,6 +135,8 @@ const char* qmm_kernel_name(int kernel_id) {
         case QMM_KERNEL_VALU: return "valu_splitfree";
         case QMM_KERNEL_MFMA_REG: return "mfma_splitfree_reg";
         case QMM_KERNEL_MFMA_PASS: return "mfma_splitfree_pass";
+        case QMM_KERNEL_MFMA_TILE16: return "mfma_splitfree_tile16";
+        case QMM_KERNEL_MFMA_TILE64: return "mfma_splitfree_tile64";
         default: return "?";
     }
 }

@@ -9,24 +9,41 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /
         case QMM_KERNEL_VALU: return M <= 64;
         case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, gs, M, K);
         case QMM_KERNEL_MFMA_PASS: return M <= 64;
+        case QMM_KERNEL_MFMA_TILE16:
+        case QMM_KERNEL_MFMA_TILE64: return mfma_tile_supports(bits, M, K);
         default: return false;
     }
 }
 
 // Crossovers measured on MI355X (graph-replayed calls over a weight stack
 // larger than the Infinity Cache; affine_quantized_gemm_amd/sweep.py):
-//   * the register-resident MFMA kernel is fastest wherever it can run
-//     (M <= 16, K <= 4096): e.g. 5.0 us vs 7.3 us (pass kernel) vs 14.2 us
-//     (VALU) at M = 6, K = N = 4096, 4-bit; 7.3 us vs 9.2 us (VALU) at M = 1,
-//     8-bit;
-//   * the pass kernel everywhere else: 15.3 us vs 18.9 us (VALU) at M = 1 on
-//     the 14336-deep down projection, 84 us vs 294 us at M = 64;
+//   * M <= 16: the register-resident MFMA kernel wherever it can run
+//     (K <= 4096): 5.0 us vs 7.4 us (pass) vs 14.2 us (VALU) at M = 6,
+//     K = N = 4096, 4-bit; the pass kernel for longer K (18.4 us vs 25.2 us
+//     for the 16-column tile kernel at M = 8 on the 4096 x 14336 down
+//     projection);
+//   * M > 16, wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
+//     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
+//     projection, 186 / 278 us vs 368 / 669 us on the 151936-column LM head;
+//   * M > 32, narrower N: the 16-column tile kernel: 46.0 / 64.7 us vs
+//     56.1 / 65.5 us (pass) at M = 36 / 64 on the down projection, 16.1 /
+//     20.3 us vs 21.6 / 21.9 us at K = N = 4096;
+//   * everything else (M = 17..32 with N < 8192, or K the tile kernels do not
+//     take): the pass kernel (37.3 us vs 47.7 us for the 16-column tiles at
+//     M = 32 on the down projection);
 //   * the VALU kernel is not selected (kept as an independent variant for
 //     measurement and cross-checks).
 // The pages' own dispatch is likewise a measured crossover in M per shape
 // (MLX issue #4720, "Root cause"; crossover near M = 6-8 on Apple parts).
 int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
-    return kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K) ? QMM_KERNEL_MFMA_REG : QMM_KERNEL_MFMA_PASS;
+    if (M <= 16)
+        return kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K) ? QMM_KERNEL_MFMA_REG
+                                                                           : QMM_KERNEL_MFMA_PASS;
+    if (kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) {
+        if (N >= 8192) return QMM_KERNEL_MFMA_TILE64;
+        if (M > 32) return QMM_KERNEL_MFMA_TILE16;
+    }
+    return QMM_KERNEL_MFMA_PASS;
 }
 
 hipError_t launch_kernel(int kid, const MatmulArgs& a) {
@@ -34,6 +51,8 @@ hipError_t launch_kernel(int kid, const MatmulArgs& a) {
         case QMM_KERNEL_VALU: return launch_valu(a);
         case QMM_KERNEL_MFMA_REG: return launch_mfma_reg(a);
         case QMM_KERNEL_MFMA_PASS: return launch_mfma_pass(a);
+        case QMM_KERNEL_MFMA_TILE16: return launch_mfma_tile(a, false);
+        case QMM_KERNEL_MFMA_TILE64: return launch_mfma_tile(a, true);
         default: return hipErrorInvalidValue;
     }
 }

@@ -26,6 +26,8 @@ struct MatmulArgs {
 hipError_t launch_valu(const MatmulArgs& a);
 hipError_t launch_mfma_reg(const MatmulArgs& a);
 hipError_t launch_mfma_pass(const MatmulArgs& a);
+hipError_t launch_mfma_tile(const MatmulArgs& a, bool wide);
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K);
+bool mfma_tile_supports(int bits, int64_t M, int64_t K);
 
 }  // namespace qmm

@@ -74,7 +74,7 @@ def supported(Q, kernel, M, bits=4, gs=64, N=64, K=512, dt=torch.float16):
     return kernel is None or Q.kernel_supported(dt, bits, gs, M, N, K, kernel)
 
 
-KERNELS = [None, 0, 1, 2]
+KERNELS = [None, 0, 1, 2, 3, 4]
 
 
 @pytest.mark.parametrize("dt,bits,gs", COMBOS)
@@ -219,3 +219,30 @@ def test_multi_tile_ragged(Q, dt, bits, gs):
     assert ok, worst
     ok, worst = run_case(Q, dt, bits, gs, 16, N, K, seed=bits * 100 + gs + 1, kernel=Q.KERNEL_MFMA_REG)
     assert ok, worst
+
+
+@pytest.mark.parametrize("kernel", [3, 4])
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 4, 64), ("bf16", 4, 32), ("f16", 4, 128), ("bf16", 6, 64),
+                                        ("f16", 6, 32), ("bf16", 8, 128), ("f16", 8, 64)])
+def test_tile_kernels(Q, kernel, dt, bits, gs):
+    """The shared-activation tile kernels: more column tiles than resident
+    workgroups (persistent walk over tiles, weight prefetch across a tile
+    boundary), a last pass with fewer k-blocks than k-groups, M across one to
+    four 16-row blocks with ragged ends, and a ragged last column tile."""
+    bn = 16 if kernel == Q.KERNEL_MFMA_TILE16 else 64
+    N = bn * 257 + 5
+    kblk = 128 if bits == 4 else 64
+    K = 16 * kblk + max(kblk, gs)   # passes of 4 (or 2) k-blocks and a short last pass
+    seed = kernel * 1000 + bits * 10 + gs
+    w = synth.normal((N, K), 0.02, dt, seed, outlier_frac=0.01)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    wq, sc, bi = (synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(),
+                  synth.from_oracle(obi, dt).cuda())
+    for M in (1, 17, 40, 64):
+        print(f"tile kernel={kernel} {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
+        x = synth.normal((M, K), 1.0, dt, seed + M)
+        y = Q.small_m(x.cuda(), wq, sc, bi, bits, gs, kernel=kernel)
+        torch.cuda.synchronize()
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+        ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+        assert ok, (M, worst)
