@@ -25,9 +25,11 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /
 //   * M > 16, wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
 //     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
 //     projection, 186 / 278 us vs 368 / 669 us on the 151936-column LM head;
-//   * M > 32, narrower N: the 16-column tile kernel: 46.0 / 64.7 us vs
-//     56.1 / 65.5 us (pass) at M = 36 / 64 on the down projection, 16.1 /
-//     20.3 us vs 21.6 / 21.9 us at K = N = 4096;
+//   * M > 32, N from 4096 (at least one 16-column tile per CU): the
+//     16-column tile kernel: 46.0 / 64.7 us vs 56.1 / 65.5 us (pass) at
+//     M = 36 / 64 on the down projection, 16.1 / 20.3 us vs 21.6 / 21.9 us at
+//     K = N = 4096; with fewer tiles than CUs it idles most of the chip
+//     (15.7 us vs 7.8 us for the pass kernel at M = 36, N = 1024);
 //   * everything else (M = 17..32 with N < 8192, or K the tile kernels do not
 //     take): the pass kernel (37.3 us vs 47.7 us for the 16-column tiles at
 //     M = 32 on the down projection);
@@ -41,7 +43,7 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
                                                                            : QMM_KERNEL_MFMA_PASS;
     if (kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) {
         if (N >= 8192) return QMM_KERNEL_MFMA_TILE64;
-        if (M > 32) return QMM_KERNEL_MFMA_TILE16;
+        if (M > 32 && N >= 4096) return QMM_KERNEL_MFMA_TILE16;
     }
     return QMM_KERNEL_MFMA_PASS;
 }

@@ -80,10 +80,23 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_digest():
+# Source files each kernel variant is compiled from (its translation unit and
+# the headers it includes): the counter summary of a kernel stays valid while
+# these are unchanged.
+KERNEL_SOURCES = {
+    "valu_splitfree": ["qmm_valu.hip"],
+    "mfma_splitfree_reg": ["qmm_mfma_reg.hip", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_pass": ["qmm_mfma_pass.hip", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_tile16": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_tile64": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
+}
+COMMON_SOURCES = ["qmm_device.hpp", "qmm_internal.hpp"]
+
+
+def kernel_source_digest(kernel_name):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "affine_quantized_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(set(KERNEL_SOURCES[kernel_name] + COMMON_SOURCES)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -367,8 +380,8 @@ def main():
     alg_mean = sum(alg.values()) / len(Ms)
     launch_us = sum(per_m.values()) / len(Ms)
     achieved = alg_mean / (launch_us * 1e-6) / 1e9
-    digest = kernel_source_digest()
     kid = args.kernel if args.kernel is not None else Q.select_kernel(tdt, bits, gs, Ms[-1], N, K)
+    digest = kernel_source_digest(Q.kernel_name(kid))
     kernels = {f"M{M}": Q.kernel_name(args.kernel if args.kernel is not None
                                       else Q.select_kernel(tdt, bits, gs, M, N, K)) for M in Ms}
 

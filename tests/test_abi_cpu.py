@@ -149,8 +149,9 @@ def test_dispatch_follows_measured_crossovers():
     """qmm_select_kernel encodes the crossovers measured on MI355X
     (affine_quantized_gemm_amd/sweep.py): M <= 16 -> the register-resident
     MFMA kernel where it runs (K <= 4096), else the pass kernel; M > 16 -> the
-    64-column tile kernel for wide N, the 16-column tile kernel for M > 32,
-    the pass kernel otherwise (and wherever the tile kernels cannot run)."""
+    64-column tile kernel for wide N, the 16-column tile kernel for M > 32
+    when N gives every CU a tile, the pass kernel otherwise (and wherever the
+    tile kernels cannot run)."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
     sel = lambda dt, b, gs, M, N, K: Q.kernel_name(Q.select_kernel(dt, b, gs, M, N, K))
@@ -162,8 +163,10 @@ def test_dispatch_follows_measured_crossovers():
     for M in (17, 24, 32, 36, 48, 64):
         assert sel(f16, 4, 64, M, 14336, 4096) == "mfma_splitfree_tile64"
         assert sel(bf16, 8, 64, M, 151936, 4096) == "mfma_splitfree_tile64"
-        for N, K in ((4096, 4096), (4096, 14336), (1024, 4096)):
+        for N, K in ((4096, 4096), (4096, 14336)):
             assert sel(f16, 4, 64, M, N, K) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        # fewer 16-column tiles than CUs: the pass kernel
+        assert sel(f16, 4, 64, M, 1024, 4096) == "mfma_splitfree_pass"
         # K that is not a whole number of 4-bit k-blocks: the pass kernel
         assert sel(f16, 4, 64, M, 14336, 4160) == "mfma_splitfree_pass"
     assert sel(f16, 6, 64, 40, 4096, 4160) == "mfma_splitfree_tile16"   # 6-bit k-blocks are 64 codes
