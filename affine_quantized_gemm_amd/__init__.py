@@ -31,6 +31,7 @@ EXPORTS = (
     "qmm_quantize", "qmm_dequantize", "qmm_small_m", "qmm_small_m_forced",
     "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
     "qmm_probe_stream_read", "qmm_probe_copy",
+    "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
 )
 
 
@@ -58,6 +59,11 @@ def _load():
         "qmm_kernel_name": (ctypes.c_char_p, [i32]),
         "qmm_probe_stream_read": (i32, [vp, i64, vp, i32, vp]),
         "qmm_probe_copy": (i32, [vp, vp, i64, vp]),
+        "qmm_small_m_ws": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "qmm_small_m_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
+        "qmm_small_m_split_forced": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp,
+                                           i32, i32]),
+        "qmm_split_plan": (i32, [i32, i32, i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -78,6 +84,10 @@ qmm_packed_words = _lib.qmm_packed_words
 qmm_kernel_supported = _lib.qmm_kernel_supported
 qmm_probe_stream_read = _lib.qmm_probe_stream_read
 qmm_probe_copy = _lib.qmm_probe_copy
+qmm_small_m_ws = _lib.qmm_small_m_ws
+qmm_small_m_workspace_bytes = _lib.qmm_small_m_workspace_bytes
+qmm_small_m_split_forced = _lib.qmm_small_m_split_forced
+qmm_split_plan = _lib.qmm_split_plan
 
 
 def strerror(status: int) -> str:
@@ -192,4 +202,50 @@ def small_m(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: tor
         _check(qmm_small_m(*args), "qmm_small_m")
     else:
         _check(qmm_small_m_forced(*args, int(kernel)), "qmm_small_m_forced")
+    return out
+
+
+def workspace_bytes(dtype, bits: int, group_size: int, M: int, N: int, K: int) -> int:
+    """Bytes of workspace :func:`small_m_ws` needs (0: it runs split-free)."""
+    r = int(_lib.qmm_small_m_workspace_bytes(_dt(dtype), bits, group_size, M, N, K))
+    if r < 0:
+        raise QmmError(r, "qmm_small_m_workspace_bytes")
+    return r
+
+
+def split_plan(dtype, bits: int, group_size: int, M: int, N: int, K: int) -> tuple[int, int]:
+    """(kernel id, K split) that :func:`small_m_ws` uses."""
+    k, s = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_lib.qmm_split_plan(_dt(dtype), bits, group_size, M, N, K, ctypes.byref(k), ctypes.byref(s)),
+           "qmm_split_plan")
+    return k.value, s.value
+
+
+def small_m_ws(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+               group_size: int, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               kernel: int | None = None, split: int | None = None, stream=None) -> torch.Tensor:
+    """As :func:`small_m`, K possibly split across workgroups with fp32 partial
+    outputs in ``workspace`` (a device tensor the caller keeps; allocated here
+    when not given).  ``kernel`` and ``split`` force the variant and split."""
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    M, K = x.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    if workspace is None:
+        need = workspace_bytes(x.dtype, bits, group_size, M, N, K) if kernel is None else \
+            max(1, int(split or 1)) * M * N * 4
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace")
+    nb = workspace.numel() * workspace.element_size()
+    args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+            biases.data_ptr(), out.data_ptr(), workspace.data_ptr(), nb, _stream(stream))
+    if kernel is None and split is None:
+        _check(qmm_small_m_ws(*args), "qmm_small_m_ws")
+    else:
+        kid = kernel if kernel is not None else split_plan(x.dtype, bits, group_size, M, N, K)[0]
+        _check(qmm_small_m_split_forced(*args, int(kid), int(split or 1)), "qmm_small_m_split_forced")
     return out

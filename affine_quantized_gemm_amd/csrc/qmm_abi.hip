@@ -113,6 +113,59 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
     return hip_status(qmm::launch_kernel(kid, a));
 }
 
+int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int* kernel_id, int* split) {
+    if (M < 0 || kernel_id == nullptr || split == nullptr) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    const qmm::SplitPlan p = qmm::plan_split(dt, bits, group_size, M, N, K);
+    *kernel_id = p.kernel;
+    *split = p.split;
+    return QMM_OK;
+}
+
+int64_t qmm_small_m_workspace_bytes(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K) {
+    if (M < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    const qmm::SplitPlan p = qmm::plan_split(dt, bits, group_size, M, N, K);
+    return p.split > 1 ? static_cast<int64_t>(p.split) * M * N * 4 : 0;
+}
+
+int qmm_small_m_split_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                             const uint32_t* wq, const void* scales, const void* biases, void* y,
+                             void* workspace, int64_t workspace_bytes, void* stream, int kernel_id, int split) {
+    int st = check_matmul(dt, bits, group_size, M, N, K, x, wq, scales, biases, y);
+    if (st != QMM_OK) return st;
+    if (split < 1 || workspace_bytes < 0) return QMM_ERR_INVALID_ARG;
+    if (!qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K)) return QMM_ERR_UNSUPPORTED;
+    const bool tile = kernel_id == QMM_KERNEL_MFMA_TILE16 || kernel_id == QMM_KERNEL_MFMA_TILE64;
+    if (split > 1 && !tile) return QMM_ERR_UNSUPPORTED;
+    const int eff = split > 1 ? qmm::tile_split(bits, K, kernel_id == QMM_KERNEL_MFMA_TILE64, split) : 1;
+    if (M == 0 || N == 0) return QMM_OK;
+    if (eff > 1) {
+        if (workspace == nullptr || workspace_bytes < static_cast<int64_t>(eff) * M * N * 4)
+            return QMM_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return QMM_ERR_MISALIGNED;
+    }
+    qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream),
+                      static_cast<float*>(workspace), eff};
+    return hip_status(qmm::launch_kernel(kernel_id, a));
+}
+
+int qmm_small_m_ws(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                   const uint32_t* wq, const void* scales, const void* biases, void* y, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+    int st = check_matmul(dt, bits, group_size, M, N, K, x, wq, scales, biases, y);
+    if (st != QMM_OK) return st;
+    if (workspace_bytes < 0) return QMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return QMM_OK;
+    const qmm::SplitPlan p = qmm::plan_split(dt, bits, group_size, M, N, K);
+    return qmm_small_m_split_forced(dt, bits, group_size, M, N, K, x, wq, scales, biases, y, workspace,
+                                    workspace_bytes, stream, p.kernel, p.split);
+}
+
 int64_t qmm_packed_words(int bits, int64_t K) {
     if (bits != 4 && bits != 6 && bits != 8) return -1;
     if (K < 0 || (K * bits) % 32 != 0) return -1;

@@ -48,6 +48,27 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     return QMM_KERNEL_MFMA_PASS;
 }
 
+// K split (workspace entry point).  Measured on MI355X (sweep.py --splits,
+// graph-replayed): the 64-column tile kernel with K split 4 ways beats every
+// split-free variant on the 4096 x 14336 down projection from M = 24 (27.1
+// vs 37.9 us at M = 24, 37.0 vs 64.2 us at M = 64) and at K = N = 4096 from
+// M = 48 (16.8 vs 17.8, 18.6 vs 20.6 us); below that, with fewer than 32
+// such tiles (k/v, N = 1024: 14.5 vs 4.9 us at M = 8) or with 8 splits the
+// partial-sum pass costs more than the activation bytes it saves.  So: split
+// when N gives 32..64 tiles of 64 columns and M >= 24 (K >= 8192) or M >= 48,
+// into min(4, 256 / tiles) parts.
+SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
+    SplitPlan p{select_kernel(dt, bits, gs, M, N, K), 1};
+    if (!kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) return p;
+    const int64_t ntiles = (N + 63) / 64;
+    if (ntiles < 32 || ntiles > 64) return p;
+    if (M < (K >= 8192 ? 24 : 48)) return p;
+    const int64_t want = 256 / ntiles < 4 ? 256 / ntiles : 4;
+    const int split = tile_split(bits, K, true, static_cast<int>(want));
+    if (split < 2) return p;
+    return SplitPlan{QMM_KERNEL_MFMA_TILE64, split};
+}
+
 hipError_t launch_kernel(int kid, const MatmulArgs& a) {
     switch (kid) {
         case QMM_KERNEL_VALU: return launch_valu(a);

@@ -15,4 +15,12 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_kernel(int kid, const MatmulArgs& a);
 
+// The variant and K split qmm_small_m_ws uses (split 1: what qmm_small_m
+// does, no workspace).
+struct SplitPlan {
+    int kernel;
+    int split;
+};
+SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K);
+
 }  // namespace qmm

@@ -21,6 +21,11 @@ struct MatmulArgs {
     const void* biases;
     void* y;
     hipStream_t stream;
+    // K split across workgroups (tile kernels only): `split` fp32 partial
+    // outputs [split][M][N] in `part`, added in order by a second kernel.
+    // split < 2: no split, `part` unused.
+    float* part;
+    int split;
 };
 
 hipError_t launch_valu(const MatmulArgs& a);
@@ -29,5 +34,8 @@ hipError_t launch_mfma_pass(const MatmulArgs& a);
 hipError_t launch_mfma_tile(const MatmulArgs& a, bool wide);
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K);
 bool mfma_tile_supports(int bits, int64_t M, int64_t K);
+// A split count made valid for the tile kernel (every split gets at least
+// one pass); the workspace holds that many partial outputs.
+int tile_split(int bits, int64_t K, bool wide, int split);
 
 }  // namespace qmm

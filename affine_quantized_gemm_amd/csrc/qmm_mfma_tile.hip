@@ -88,7 +88,8 @@ __device__ __forceinline__ uint16_t unit_half(const uint32_t (&v)[SW], int p) {
 template <int DT, int BITS, int GS, int CW, int NT, int KW_, int D>
 __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ part, int M, int64_t N,
+    int64_t K) {
     using F = Fmt<DT, BITS, GS>;
     using TF = TileFmt<DT, BITS, GS, CW, NT, KW_>;
     using Slot = TileSlot<DT, BITS, GS, NT>;
@@ -105,9 +106,15 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
 
     const int64_t nkb = K / F::KBLK;
     const int P = static_cast<int>((nkb + KW - 1) / KW);
+    // K split over gridDim.y workgroups: split s takes passes [pb, pe) of
+    // every tile and leaves fp32 partial tiles in `part` ([split][M][N]);
+    // the host makes every split non-empty.  Unsplit: pb = 0, pe = P.
+    const int PP = (P + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
+    const int pb = static_cast<int>(blockIdx.y) * PP;
+    const int pe = min(P, pb + PP);
     const int64_t ntiles = (N + TF::BN - 1) / TF::BN;
     const int64_t my_tiles = (ntiles - 1 - static_cast<int64_t>(blockIdx.x)) / gridDim.x + 1;
-    const int64_t n_it = my_tiles * P;
+    const int64_t n_it = my_tiles * (pe - pb);
 
     if (wave >= TF::CWAVES) {
         // ---- loader wavefronts: activation blocks -> LDS ----
@@ -163,12 +170,12 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
         // issues chunk it+1 and waits for it before the next barrier.  Three
         // buffers: iteration it waits for chunk it+1 (issued an iteration
         // earlier), then issues chunk it+2 into the buffer chunk it-1 used.
-        int ipass = 0, ibuf = 0;
+        int ipass = pb, ibuf = 0;
         int64_t iss = 0;
         auto issue_next = [&]() {
             if (iss < n_it) {
                 issue(ipass, ibuf);
-                ipass = ipass + 1 == P ? 0 : ipass + 1;
+                ipass = ipass + 1 == pe ? pb : ipass + 1;
                 ibuf = ibuf + 1 == nb ? 0 : ibuf + 1;
                 ++iss;
             }
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
         issue_next();
         if (nb == 3) issue_next();
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        int pass = 0;
+        int pass = pb;
         for (int64_t it = 0; it < n_it; ++it) {
             __syncthreads();  // chunk `it` is in LDS; chunk it-1's buffer is free
             if (nb == 2) {
@@ -186,12 +193,12 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 issue_next();
             }
-            if (pass == P - 1) {
+            if (pass == pe - 1) {
                 // the compute wavefronts' ordered tile reduction
 #pragma unroll
                 for (int st = 0; st < KW - 1; ++st) __syncthreads();
             }
-            pass = pass + 1 == P ? 0 : pass + 1;
+            pass = pass + 1 == pe ? pb : pass + 1;
         }
         return;
     }
@@ -336,7 +343,12 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
                             } else {
                                 const int row = 16 * rb + 4 * jj + q;
                                 const int64_t col = c0 + 16 * (cw * NT + nt) + c;
-                                if (row < M && col < N) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
+                                if (row < M && col < N) {
+                                    if (part)
+                                        part[(static_cast<int64_t>(blockIdx.y) * M + row) * N + col] = v;
+                                    else
+                                        y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
+                                }
                             }
                         }
                 }
@@ -355,13 +367,13 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
     Slot ring[D];
     const int64_t tstep = gridDim.x;
     int64_t tile = blockIdx.x;
-    int pass = 0;
+    int pass = pb;
     int64_t ptile = tile;
-    int ppass = 0;
+    int ppass = pb;
     int64_t pit = 0;
     auto advance = [&](int64_t& t, int& p) {
-        if (++p == P) {
-            p = 0;
+        if (++p == pe) {
+            p = pb;
             t += tstep;
         }
     };
@@ -394,11 +406,23 @@ __global__ __launch_bounds__(64 * (CW * KW_ + TILE_LOADERS)) void mfma_tile_kern
                 ++pit;
             }
             if (it + u < n_it) {
-                if (pass == P - 1) finish_tile(tile);
+                if (pass == pe - 1) finish_tile(tile);
                 advance(tile, pass);
             }
         }
     }
+}
+
+// y = the split partial outputs added in split order (deterministic), then
+// rounded once to dt.  part is [S][M*N] fp32.
+template <int DT>
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ y, int S, int64_t mn) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= mn) return;
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[static_cast<int64_t>(s) * mn + i];
+    y[i] = DtOps<DT>::rne(v);
 }
 
 template <int DT, int BITS, int GS, int CW, int NT, int KW, int D>
@@ -406,17 +430,26 @@ hipError_t launch_tile_cfg(const MatmulArgs& a) {
     using TF = TileFmt<DT, BITS, GS, CW, NT, KW>;
     const int rb = static_cast<int>((a.M + 15) / 16);
     const int64_t ntiles = (a.N + TF::BN - 1) / TF::BN;
-    // one workgroup per CU (its LDS use is most of a CU's)
-    const int64_t gx = ntiles < 256 ? ntiles : 256;
+    const int S = a.split > 1 ? a.split : 1;
+    // about one workgroup per CU (its LDS use is most of a CU's), the K
+    // splits of a column slot side by side in gridDim.y
+    const int64_t slots = 256 / S > 1 ? 256 / S : 1;
+    const int64_t gx = ntiles < slots ? ntiles : slots;
     const size_t lds = static_cast<size_t>(TF::lds_bytes(rb));
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>), dim3(static_cast<unsigned>(gx)),
-                       dim3(64 * TF::WAVES), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
-                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
-                       static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
+    hipLaunchKernelGGL((mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>),
+                       dim3(static_cast<unsigned>(gx), static_cast<unsigned>(S)), dim3(64 * TF::WAVES), lds,
+                       a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
+                       static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y),
+                       S > 1 ? a.part : nullptr, static_cast<int>(a.M), a.N, a.K);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const int64_t mn = a.M * a.N;
+    hipLaunchKernelGGL((reduce_partials_kernel<DT>), dim3(static_cast<unsigned>((mn + 255) / 256)), dim3(256), 0,
+                       a.stream, a.part, static_cast<uint16_t*>(a.y), S, mn);
     return hipGetLastError();
 }
 
@@ -431,6 +464,16 @@ hipError_t launch_tile_t(const MatmulArgs& a, bool wide) {
 }
 
 }  // namespace
+
+int tile_split(int bits, int64_t K, bool wide, int split) {
+    const int64_t kblk = bits == 4 ? 128 : 64;
+    const int64_t kw = wide ? 2 : 4;  // k-blocks per pass of the two shapes (launch_tile_t)
+    const int64_t P = (K / kblk + kw - 1) / kw;
+    int64_t S = split < 1 ? 1 : split;
+    if (S > P) S = P;
+    const int64_t PP = (P + S - 1) / S;
+    return static_cast<int>((P + PP - 1) / PP);
+}
 
 bool mfma_tile_supports(int bits, int64_t M, int64_t K) {
     const int64_t kblk = bits == 4 ? 128 : 64;

@@ -8,7 +8,7 @@ events on the replay stream.  The fastest
 variant per (shape, M) is what ``qmm_select_kernel`` should return; the
 measured table is the source of the crossovers compiled into the dispatch.
 
-    python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...]
+    python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...] [--splits]
 
 The pages' own dispatch story is a crossover curve in M, measured per shape
 (MLX issue #4720, "Root cause" and the M-sweep table under "Measurements").
@@ -73,7 +73,10 @@ def time_calls(fn, n_calls, reps=5):
     return best
 
 
-def sweep_shape(name, ms, stack_mib):
+SPLITS = ((3, 2), (3, 4), (4, 2), (4, 4), (4, 8))   # (tile kernel id, K split) timed with --splits
+
+
+def sweep_shape(name, ms, stack_mib, splits=False):
     N, K, dt, bits, gs = SHAPES[name]
     tdt = synth.TORCH_DT[dt]
     B = weight_bytes(N, K, bits, gs)
@@ -97,13 +100,36 @@ def sweep_shape(name, ms, stack_mib):
                     Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=kid)
 
             res[Q.kernel_name(kid)] = round(time_calls(run, len(stack)), 3)
+        ws_res = {}
+        if splits:
+            ws = torch.empty((64 * M * N * 4 + 16,), dtype=torch.uint8, device="cuda")
+            for kid, sp in SPLITS:
+                if not Q.kernel_supported(tdt, bits, gs, M, N, K, kid):
+                    continue
+
+                def run_s(kid=kid, sp=sp):
+                    for (wq, sc, bi) in stack:
+                        Q.small_m_ws(x, wq, sc, bi, bits, gs, workspace=ws, out=y, kernel=kid, split=sp)
+
+                ws_res[f"{Q.kernel_name(kid)}/k{sp}"] = round(time_calls(run_s, len(stack)), 3)
+            pk, psplit = Q.split_plan(tdt, bits, gs, M, N, K)
+            if psplit > 1:
+                def run_p():
+                    for (wq, sc, bi) in stack:
+                        Q.small_m_ws(x, wq, sc, bi, bits, gs, workspace=ws, out=y)
+                ws_res["planned_ws"] = round(time_calls(run_p, len(stack)), 3)
+            del ws
         best = min(res, key=res.get)
         sel = Q.kernel_name(Q.select_kernel(tdt, bits, gs, M, N, K))
-        rows.append({"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "M": M, "us": res,
-                     "fastest": best, "selected": sel,
-                     "selected_gbs": round(B / (res[sel] * 1e-6) / 1e9, 1)})
+        row = {"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "M": M, "us": res,
+               "fastest": best, "selected": sel, "selected_gbs": round(B / (res[sel] * 1e-6) / 1e9, 1)}
+        if splits:
+            row["split_us"] = ws_res
+            row["plan"] = list(Q.split_plan(tdt, bits, gs, M, N, K))
+        rows.append(row)
         print(f"{name:8s} M={M:3d}  " + "  ".join(f"{k} {v:8.2f}" for k, v in res.items())
-              + f"   fastest {best}   selected {sel}", flush=True)
+              + f"   fastest {best}   selected {sel}"
+              + ("   | " + "  ".join(f"{k} {v:.2f}" for k, v in ws_res.items()) if ws_res else ""), flush=True)
     del stack
     torch.cuda.empty_cache()
     return rows
@@ -115,11 +141,12 @@ def main():
     p.add_argument("--ms", default=",".join(map(str, MS)))
     p.add_argument("--stack-mib", type=int, default=576)
     p.add_argument("--json", default=None)
+    p.add_argument("--splits", action="store_true", help="also time K splits of the tile kernels (workspace path)")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
     rows = []
     for name in a.shapes.split(","):
-        rows += sweep_shape(name, ms, a.stack_mib)
+        rows += sweep_shape(name, ms, a.stack_mib, a.splits)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(rows, f, indent=1)

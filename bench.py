@@ -71,6 +71,8 @@ def parse():
     p.add_argument("--workload", default="verify", choices=sorted(WORKLOADS))
     p.add_argument("--stack-mib", type=int, default=576, help="total weight bytes of the cycled stack")
     p.add_argument("--kernel", type=int, default=None, help="force a kernel variant")
+    p.add_argument("--workspace", action="store_true",
+                   help="call qmm_small_m_ws (K split where its plan says so) instead of qmm_small_m")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extras", action="store_true",
@@ -338,11 +340,19 @@ def main():
     # graph, so that a graph launch is not charged to a handful of calls
     P = max(1, -(-32 // S))
 
+    # --workspace: the workspace entry point (K split across workgroups where
+    # its plan says so), with the workspace allocated here, outside the timing
+    wss = {M: torch.empty((max(16, Q.workspace_bytes(tdt, bits, gs, M, N, K)),), dtype=torch.uint8, device=dev)
+           for M in Ms} if args.workspace else {}
+
     def calls(M):
         x, y = xs[M], ys[M]
         for _ in range(P):
             for (wq, sc, bi) in stack:
-                Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
+                if args.workspace:
+                    Q.small_m_ws(x, wq, sc, bi, bits, gs, workspace=wss[M], out=y)
+                else:
+                    Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
 
     # The step's launches are captured once per M into a HIP graph and the
     # graphs are replayed: the calls are launch-bound from Python (a few us
@@ -380,10 +390,16 @@ def main():
     alg_mean = sum(alg.values()) / len(Ms)
     launch_us = sum(per_m.values()) / len(Ms)
     achieved = alg_mean / (launch_us * 1e-6) / 1e9
-    kid = args.kernel if args.kernel is not None else Q.select_kernel(tdt, bits, gs, Ms[-1], N, K)
+    def chosen(M):
+        if args.workspace:
+            k, sp = Q.split_plan(tdt, bits, gs, M, N, K)
+            return Q.kernel_name(k) + (f" (K split {sp})" if sp > 1 else "")
+        return Q.kernel_name(args.kernel if args.kernel is not None else Q.select_kernel(tdt, bits, gs, M, N, K))
+
+    kid = args.kernel if args.kernel is not None else (
+        Q.split_plan(tdt, bits, gs, Ms[-1], N, K)[0] if args.workspace else Q.select_kernel(tdt, bits, gs, Ms[-1], N, K))
     digest = kernel_source_digest(Q.kernel_name(kid))
-    kernels = {f"M{M}": Q.kernel_name(args.kernel if args.kernel is not None
-                                      else Q.select_kernel(tdt, bits, gs, M, N, K)) for M in Ms}
+    kernels = {f"M{M}": chosen(M) for M in Ms}
 
     extras = {}
     if not args.no_extras:
@@ -411,6 +427,7 @@ def main():
                                f"{S} distinct matrices ({S * B / 2**20:.0f} MiB) cycled per call, "
                                f"{P} pass(es) over them per M per step",
                    "workload_name": args.workload,
+                   "entry": "qmm_small_m_ws" if args.workspace else "qmm_small_m",
                    "M": list(Ms), "N": N, "K": K, "bits": bits, "group_size": gs, "stack": S, "passes": P,
                    "kernel": kernels},
         "us_per_call": {f"M{M}": round(per_m[M], 3) for M in Ms},

@@ -41,7 +41,8 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *     No entry point synchronizes, allocates memory or keeps a pointer
  *     after it returns; the caller keeps buffers alive until the stream has
- *     passed the call.  Entry points are thread-safe.
+ *     passed the call (scratch, where a variant needs it, is a
+ *     caller-provided workspace).  Entry points are thread-safe.
  *   - Arguments are validated before any HIP call.  Return values:
  *       QMM_OK               success (also for empty problems: M == 0 or
  *                            N == 0 launch nothing and may pass NULL)
@@ -120,6 +121,48 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
 int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
                        const void* x, const uint32_t* wq, const void* scales,
                        const void* biases, void* y, void* stream, int kernel_id);
+
+/*
+ * K split across workgroups, for the shapes with few column tiles per CU
+ * (the batched-decode down projection: N = 4096, K = 14336).  A split-free
+ * kernel makes every CU read the whole activation matrix (M*K*2 bytes) for
+ * its columns; with K split S ways a CU reads 1/S of it.  The partial
+ * outputs (fp32, [S][M][N]) go to a caller-provided workspace and a second
+ * kernel adds them in split order and rounds once, so results stay
+ * deterministic.  This splits K the way MLX issue #4720 ("Root cause")
+ * describes qmm_splitk; there it is the slow path on Apple parts, here it is
+ * taken only where it measured faster.
+ *
+ * qmm_small_m_workspace_bytes: bytes qmm_small_m_ws needs for this problem
+ * (0: it runs split-free, exactly as qmm_small_m), or a negative status.
+ * Pure host logic.
+ *
+ * qmm_small_m_ws: as qmm_small_m, with `workspace` caller-owned device
+ * memory of `workspace_bytes` >= qmm_small_m_workspace_bytes(...) bytes,
+ * 16-byte aligned (may be NULL when that is 0).  The workspace is
+ * overwritten by the call and must not alias x, wq, scales, biases or y;
+ * two calls in flight at once need two workspaces.  Too small or NULL when
+ * needed -> QMM_ERR_INVALID_ARG; misaligned -> QMM_ERR_MISALIGNED.  Nothing
+ * is allocated.
+ *
+ * qmm_small_m_split_forced: the same with the variant and split forced
+ * (measurement and tests).  split >= 1; split > 1 needs a TILE variant and
+ * is reduced to the largest count that gives every split part of K; the
+ * workspace must hold that many [M][N] fp32 outputs.
+ *
+ * qmm_split_plan: the variant and split qmm_small_m_ws uses.  Pure host
+ * logic.
+ */
+int64_t qmm_small_m_workspace_bytes(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K);
+int qmm_small_m_ws(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                   const void* x, const uint32_t* wq, const void* scales,
+                   const void* biases, void* y, void* workspace, int64_t workspace_bytes, void* stream);
+int qmm_small_m_split_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                             const void* x, const uint32_t* wq, const void* scales,
+                             const void* biases, void* y, void* workspace, int64_t workspace_bytes,
+                             void* stream, int kernel_id, int split);
+int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                   int* kernel_id, int* split);
 
 /* The variant qmm_small_m runs for this problem (a qmm_kernel value), or a
  * negative status if the problem is not supported.  Pure host logic. */

@@ -170,3 +170,50 @@ def test_dispatch_follows_measured_crossovers():
         # K that is not a whole number of 4-bit k-blocks: the pass kernel
         assert sel(f16, 4, 64, M, 14336, 4160) == "mfma_splitfree_pass"
     assert sel(f16, 6, 64, 40, 4096, 4160) == "mfma_splitfree_tile16"   # 6-bit k-blocks are 64 codes
+
+
+def test_split_plan_and_workspace_bytes():
+    """The K-split plan of qmm_small_m_ws (crossovers measured with sweep.py
+    --splits): the 64-column tile kernel split min(4, 256 / tiles) ways when N
+    gives 32..64 such tiles and M >= 24 (K >= 8192) or M >= 48; otherwise no
+    split and no workspace (exactly qmm_small_m)."""
+    import torch
+    f16, bf16 = torch.float16, torch.bfloat16
+    # down projection 4096 x 14336: 64 tiles -> 4 splits of 28 passes (7 each), from M = 24
+    for M in (24, 32, 36, 48, 64):
+        assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+        assert Q.workspace_bytes(f16, 4, 64, M, 4096, 14336) == 4 * M * 4096 * 4
+    # K = N = 4096: from M = 48
+    assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
+    # N = 2048: 32 tiles -> 4 splits (capped)
+    assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+    # no split: small M, few tiles (k/v), many tiles (gate/up, LM head), K the tile kernels do not take
+    for args in ((f16, 4, 64, 16, 4096, 14336), (f16, 4, 64, 36, 4096, 4096), (f16, 4, 64, 64, 1024, 4096),
+                 (f16, 4, 64, 64, 14336, 4096), (bf16, 4, 64, 64, 151936, 4096), (f16, 4, 64, 64, 4096, 14400),
+                 (f16, 4, 64, 6, 4096, 4096)):
+        k, s = Q.split_plan(*args)
+        assert s == 1 and k == Q.select_kernel(*args) and Q.workspace_bytes(*args) == 0, args
+    assert Q.qmm_small_m_workspace_bytes(0, 4, 64, 65, 4096, 4096) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_workspace_bytes(0, 4, 64, -1, 4096, 4096) == Q.QMM_ERR_INVALID_ARG
+
+
+def test_split_entry_validation():
+    """Errors of the workspace entry points are returned before any HIP call
+    (fake addresses, no GPU)."""
+    f16 = Q.QMM_F16
+    base = (f16, 4, 64, 32, 4096, 14336, A, A, A, A, A)
+    need = 4 * 32 * 4096 * 4
+    # workspace too small, missing, or misaligned
+    assert Q.qmm_small_m_ws(*base, A, need - 4, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_small_m_ws(*base, None, need, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_small_m_ws(*base, MIS, need, None) == Q.QMM_ERR_MISALIGNED
+    assert Q.qmm_small_m_ws(*base, A, -1, None) == Q.QMM_ERR_INVALID_ARG
+    # forced: split < 1, a split on a kernel that cannot split, a kernel that cannot run the shape
+    assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_TILE64, 0) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_PASS, 2) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_REG, 1) == Q.QMM_ERR_UNSUPPORTED
+    # the workspace a forced split needs is the reduced split's: 28 passes, split 5 -> 6 passes each -> 5 splits
+    assert Q.qmm_small_m_split_forced(*base, A, 5 * 32 * 4096 * 4 - 4, None, Q.KERNEL_MFMA_TILE16, 5) == \
+        Q.QMM_ERR_INVALID_ARG
+    # empty problems: OK, nothing launched
+    assert Q.qmm_small_m_ws(f16, 4, 64, 0, 4096, 14336, None, None, None, None, None, None, 0, None) == Q.QMM_OK

@@ -246,3 +246,69 @@ def test_tile_kernels(Q, kernel, dt, bits, gs):
         yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
         ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
         assert ok, (M, worst)
+
+
+@pytest.mark.parametrize("kernel", [3, 4])
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 4, 64), ("bf16", 4, 32), ("bf16", 6, 128), ("f16", 8, 64)])
+def test_split_k(Q, kernel, dt, bits, gs):
+    """K split across workgroups (workspace path): splits that divide the
+    passes evenly and unevenly (the last split shorter), a split larger than
+    the passes (reduced), a short last pass, M across row blocks, ragged N;
+    deterministic across repeats."""
+    kblk = 128 if bits == 4 else 64
+    kw = 2 if kernel == Q.KERNEL_MFMA_TILE64 else 4
+    K = (9 * kw) * kblk + max(kblk, gs)      # 9 full passes + a short one
+    N = 64 * 5 + 7
+    seed = 5000 + kernel * 100 + bits * 10 + gs
+    w = synth.normal((N, K), 0.02, dt, seed, outlier_frac=0.01)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    wq, sc, bi = (synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(),
+                  synth.from_oracle(obi, dt).cuda())
+    for M in (1, 17, 64):
+        x = synth.normal((M, K), 1.0, dt, seed + M)
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+        xc = x.cuda()
+        for split in (2, 3, 4, 64):
+            print(f"split kernel={kernel} {dt} b{bits} gs{gs} M={M} N={N} K={K} split={split}", flush=True)
+            ws = torch.empty((split * M * N * 4 + 16,), dtype=torch.uint8, device="cuda")
+            y = Q.small_m_ws(xc, wq, sc, bi, bits, gs, workspace=ws, kernel=kernel, split=split)
+            torch.cuda.synchronize()
+            ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+            assert ok, (M, split, worst)
+            y2 = Q.small_m_ws(xc, wq, sc, bi, bits, gs, workspace=ws, kernel=kernel, split=split)
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (M, split)
+
+
+@pytest.mark.parametrize("M", [24, 36, 64])
+def test_small_m_ws_planned(Q, M):
+    """qmm_small_m_ws with its own plan on the down projection (4096 x 14336,
+    split 4) against the oracle, and equal to qmm_small_m within tolerance of
+    the oracle too; a plan without a split takes no workspace."""
+    dt, bits, gs, N, K = "f16", 4, 64, 4096, 14336
+    assert Q.split_plan(torch.float16, bits, gs, M, N, K)[1] > 1
+    w = synth.normal((N, K), 0.02, dt, 900 + M)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    wq, sc, bi = (synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(),
+                  synth.from_oracle(obi, dt).cuda())
+    x = synth.normal((M, K), 1.0, dt, 901 + M)
+    need = Q.workspace_bytes(torch.float16, bits, gs, M, N, K)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    print(f"ws planned M={M} need={need}", flush=True)
+    y = Q.small_m_ws(x.cuda(), wq, sc, bi, bits, gs, workspace=ws)
+    torch.cuda.synchronize()
+    yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+    ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+    assert ok, worst
+    # no split planned (verify rows): no workspace needed, same path as qmm_small_m
+    assert Q.workspace_bytes(torch.float16, bits, gs, 6, 4096, 4096) == 0
+
+
+def test_small_m_ws_errors(Q):
+    w = synth.normal((4096, 14336), 0.02, "f16", 1).cuda()
+    wq, sc, bi = Q.quantize(w, 4, 64)
+    x = torch.ones((32, 14336), dtype=torch.float16, device="cuda")
+    need = Q.workspace_bytes(torch.float16, 4, 64, 32, 4096, 14336)
+    small = torch.empty((need - 64,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(Q.QmmError) as e:
+        Q.small_m_ws(x, wq, sc, bi, 4, 64, workspace=small)
+    assert e.value.status == Q.QMM_ERR_INVALID_ARG
