@@ -140,9 +140,11 @@ int qmm_small_m_split_forced(int dt, int bits, int group_size, int64_t M, int64_
     if (st != QMM_OK) return st;
     if (split < 1 || workspace_bytes < 0) return QMM_ERR_INVALID_ARG;
     if (!qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K)) return QMM_ERR_UNSUPPORTED;
-    const bool tile = kernel_id == QMM_KERNEL_MFMA_TILE16 || kernel_id == QMM_KERNEL_MFMA_TILE64;
-    if (split > 1 && !tile) return QMM_ERR_UNSUPPORTED;
-    const int eff = split > 1 ? qmm::tile_split(bits, K, kernel_id == QMM_KERNEL_MFMA_TILE64, split) : 1;
+    const int cfg = kernel_id == QMM_KERNEL_MFMA_TILE16  ? qmm::TILE_CFG_16
+                    : kernel_id == QMM_KERNEL_MFMA_TILE64 ? qmm::TILE_CFG_64
+                                                          : -1;
+    if (split > 1 && cfg < 0) return QMM_ERR_UNSUPPORTED;
+    const int eff = split > 1 ? qmm::tile_split(bits, K, cfg, split) : 1;
     if (M == 0 || N == 0) return QMM_OK;
     if (eff > 1) {
         if (workspace == nullptr || workspace_bytes < static_cast<int64_t>(eff) * M * N * 4)

@@ -9,8 +9,8 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /
         case QMM_KERNEL_VALU: return M <= 64;
         case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, gs, M, K);
         case QMM_KERNEL_MFMA_PASS: return M <= 64;
-        case QMM_KERNEL_MFMA_TILE16:
-        case QMM_KERNEL_MFMA_TILE64: return mfma_tile_supports(bits, M, K);
+        case QMM_KERNEL_MFMA_TILE16: return mfma_tile_supports(bits, M, K, TILE_CFG_16);
+        case QMM_KERNEL_MFMA_TILE64: return mfma_tile_supports(bits, M, K, TILE_CFG_64);
         default: return false;
     }
 }
@@ -64,7 +64,7 @@ SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) 
     if (ntiles < 32 || ntiles > 64) return p;
     if (M < (K >= 8192 ? 24 : 48)) return p;
     const int64_t want = 256 / ntiles < 4 ? 256 / ntiles : 4;
-    const int split = tile_split(bits, K, true, static_cast<int>(want));
+    const int split = tile_split(bits, K, TILE_CFG_64, static_cast<int>(want));
     if (split < 2) return p;
     return SplitPlan{QMM_KERNEL_MFMA_TILE64, split};
 }
@@ -74,8 +74,8 @@ hipError_t launch_kernel(int kid, const MatmulArgs& a) {
         case QMM_KERNEL_VALU: return launch_valu(a);
         case QMM_KERNEL_MFMA_REG: return launch_mfma_reg(a);
         case QMM_KERNEL_MFMA_PASS: return launch_mfma_pass(a);
-        case QMM_KERNEL_MFMA_TILE16: return launch_mfma_tile(a, false);
-        case QMM_KERNEL_MFMA_TILE64: return launch_mfma_tile(a, true);
+        case QMM_KERNEL_MFMA_TILE16: return launch_mfma_tile(a, TILE_CFG_16);
+        case QMM_KERNEL_MFMA_TILE64: return launch_mfma_tile(a, TILE_CFG_64);
         default: return hipErrorInvalidValue;
     }
 }

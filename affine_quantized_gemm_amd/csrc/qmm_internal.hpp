@@ -31,11 +31,13 @@ struct MatmulArgs {
 hipError_t launch_valu(const MatmulArgs& a);
 hipError_t launch_mfma_reg(const MatmulArgs& a);
 hipError_t launch_mfma_pass(const MatmulArgs& a);
-hipError_t launch_mfma_tile(const MatmulArgs& a, bool wide);
+// tile kernel shapes (columns per workgroup tile)
+enum { TILE_CFG_16 = 0, TILE_CFG_64 = 1 };
+hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg);
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K);
-bool mfma_tile_supports(int bits, int64_t M, int64_t K);
+bool mfma_tile_supports(int bits, int64_t M, int64_t K, int cfg);
 // A split count made valid for the tile kernel (every split gets at least
 // one pass); the workspace holds that many partial outputs.
-int tile_split(int bits, int64_t K, bool wide, int split);
+int tile_split(int bits, int64_t K, int cfg, int split);
 
 }  // namespace qmm

@@ -453,21 +453,26 @@ hipError_t launch_tile_cfg(const MatmulArgs& a) {
     return hipGetLastError();
 }
 
-// Both shapes run 4 compute wavefronts and 2 loaders (6 wavefronts: at most
-// 2 per SIMD, so 256 VGPRs each).  16-column tiles: one column tile per
-// compute wavefront, 4 k-blocks per pass, weights 8 iterations ahead.
-// 64-column tiles: two column groups of two tiles each, 2 k-blocks per pass,
-// weights 4 iterations ahead.
+// Every shape runs 4 compute wavefronts and 2 loaders (6 wavefronts: at
+// most 2 per SIMD, so 256 VGPRs each):
+//   TILE16:  one 16-column tile per compute wavefront, 4 k-blocks per pass,
+//            weights 8 iterations ahead;
+//   TILE64:  two column groups of two tiles, 2 k-blocks per pass, 4 ahead.
+// (KW per shape is also in tile_split.)
 template <int DT, int BITS, int GS>
-hipError_t launch_tile_t(const MatmulArgs& a, bool wide) {
-    return wide ? launch_tile_cfg<DT, BITS, GS, 2, 2, 2, 4>(a) : launch_tile_cfg<DT, BITS, GS, 1, 1, 4, 8>(a);
+hipError_t launch_tile_t(const MatmulArgs& a, int cfg) {
+    switch (cfg) {
+        case TILE_CFG_16: return launch_tile_cfg<DT, BITS, GS, 1, 1, 4, 8>(a);
+        case TILE_CFG_64: return launch_tile_cfg<DT, BITS, GS, 2, 2, 2, 4>(a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-int tile_split(int bits, int64_t K, bool wide, int split) {
+int tile_split(int bits, int64_t K, int cfg, int split) {
     const int64_t kblk = bits == 4 ? 128 : 64;
-    const int64_t kw = wide ? 2 : 4;  // k-blocks per pass of the two shapes (launch_tile_t)
+    const int64_t kw = cfg == TILE_CFG_16 ? 4 : 2;  // k-blocks per pass (launch_tile_t)
     const int64_t P = (K / kblk + kw - 1) / kw;
     int64_t S = split < 1 ? 1 : split;
     if (S > P) S = P;
@@ -475,14 +480,14 @@ int tile_split(int bits, int64_t K, bool wide, int split) {
     return static_cast<int>((P + PP - 1) / PP);
 }
 
-bool mfma_tile_supports(int bits, int64_t M, int64_t K) {
+bool mfma_tile_supports(int bits, int64_t M, int64_t K, int /*cfg*/) {
     const int64_t kblk = bits == 4 ? 128 : 64;
     // (K <= 2^24 keeps every activation byte offset within 32 bits)
     return M >= 1 && M <= 16 * TILE_RBM && K % kblk == 0 && K <= (int64_t{1} << 24);
 }
 
-hipError_t launch_mfma_tile(const MatmulArgs& a, bool wide) {
-#define TCALL(D, B, G) launch_tile_t<D, B, G>(a, wide)
+hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg) {
+#define TCALL(D, B, G) launch_tile_t<D, B, G>(a, cfg)
     switch (a.dt * 100 + a.bits * 10 + a.gs / 32) {
         case 41: return TCALL(0, 4, 32);   case 42: return TCALL(0, 4, 64);   case 44: return TCALL(0, 4, 128);
         case 61: return TCALL(0, 6, 32);   case 62: return TCALL(0, 6, 64);   case 64: return TCALL(0, 6, 128);

@@ -229,7 +229,7 @@ def test_tile_kernels(Q, kernel, dt, bits, gs):
     workgroups (persistent walk over tiles, weight prefetch across a tile
     boundary), a last pass with fewer k-blocks than k-groups, M across one to
     four 16-row blocks with ragged ends, and a ragged last column tile."""
-    bn = 16 if kernel == Q.KERNEL_MFMA_TILE16 else 64
+    bn = {Q.KERNEL_MFMA_TILE16: 16, Q.KERNEL_MFMA_TILE64: 64}[kernel]
     N = bn * 257 + 5
     kblk = 128 if bits == 4 else 64
     K = 16 * kblk + max(kblk, gs)   # passes of 4 (or 2) k-blocks and a short last pass
@@ -256,7 +256,7 @@ def test_split_k(Q, kernel, dt, bits, gs):
     the passes (reduced), a short last pass, M across row blocks, ragged N;
     deterministic across repeats."""
     kblk = 128 if bits == 4 else 64
-    kw = 2 if kernel == Q.KERNEL_MFMA_TILE64 else 4
+    kw = {Q.KERNEL_MFMA_TILE16: 4, Q.KERNEL_MFMA_TILE64: 2}[kernel]
     K = (9 * kw) * kblk + max(kblk, gs)      # 9 full passes + a short one
     N = 64 * 5 + 7
     seed = 5000 + kernel * 100 + bits * 10 + gs
