@@ -109,6 +109,59 @@ __host__ __device__ constexpr bool reg_coop() {
 }
 __host__ __device__ inline int64_t sb_lds_bytes(int64_t G) { return 4 * 16 * sb_row_bytes(G); }
 
+// Weights through LDS (multi-tile 4-bit kernels).  Loaded straight into
+// registers, a wavefront's slice of a tile arrives as 16 rows x 64 bytes per
+// instruction -- the matrix-core layout puts the 16 tile columns on
+// consecutive lanes -- and half-line requests cap a long stream near 5.7 TB/s
+// on MI355X against 6.7-6.9 TB/s for whole 128-byte lines.  Here each
+// wavefront brings its slice in with direct global-to-LDS loads whose
+// consecutive lanes cover whole lines, into a ring of DMA_SLOTS slots of its
+// own, and reads its fragments from there; the prefetch ring then costs LDS
+// instead of registers.  A tile's slot is read into registers before the
+// slot is refilled, so DMA_SLOTS tiles are in flight during the compute.
+// Activations are read in fragment order once per kernel (no staging area).
+template <int DT, int BITS, int GS, int KPW, bool VEC, bool MULTI>
+__host__ __device__ constexpr bool reg_dma() {
+    return MULTI && VEC && BITS == 4;
+}
+// bytes of one slot: 16 rows x the wavefront's KPW k-blocks
+template <int DT, int BITS, int GS, int KPW>
+__host__ __device__ constexpr int dma_slot_bytes() {
+    return 16 * KPW * Fmt<DT, BITS, GS>::KBLK * BITS / 8;
+}
+constexpr int DMA_WAVE_LDS = 2048;  // per wavefront: the two partial-tile buffers
+constexpr int DMA_SLOTS = 3;        // weight slots per wavefront (tiles in flight)
+// Scale/bias blocks of the DMA form, DMA_SLOTS + 1 of them (a block is read
+// by every wavefront, so it is refilled only after the next barrier): the
+// tile's 16 rows of scales then of biases, rows of 2G bytes (unpadded) whose
+// 16-byte pieces are swizzled like the weight slots.
+__host__ __device__ inline int64_t dma_sb_block_bytes(int64_t G) { return 2 * 16 * 2 * G; }
+
+// One direct global-to-LDS load: 16 bytes per active lane, lane q to
+// lds_dst + 16 q, non-temporal.  Written as assembly on purpose: for a
+// global-to-LDS load the compiler knows of, it waits for every such load
+// before any later LDS read, which would drain the prefetch ring each tile.
+// Callers wait explicitly (s_waitcnt vmcnt, in-order retirement).  M0 (the
+// LDS address) is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// base: a 64-bit address, the same in every lane (moved to scalar
+// registers here); voff: this lane's byte offset from it; m0: the LDS byte
+// address of lane 0's 16 bytes (the same in every lane).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0) {
+    // (readfirstlane returns a signed int: each half goes through uint32_t so
+    // that widening cannot sign-extend the low word over the high one)
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(sb)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // W wavefronts per workgroup; wavefront w owns the KPW consecutive k-blocks
 // [w*KPW, (w+1)*KPW) of K.  One workgroup owns a tile of 16 columns at a
 // time and walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...; the loads of
@@ -136,7 +189,9 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     using Regs = TileRegs<VEC, NGW, KPW, F::SEG_WORDS, F::PORTIONS>;
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int XS_ROW = xs_row_elems(KPW, F::KBLK);
-    const int wave_lds = wave_lds_bytes(M, KPW, F::KBLK);
+    constexpr bool DMA = reg_dma<DT, BITS, GS, KPW, VEC, MULTI>();
+    static_assert(!DMA || COOP, "the weight ring carries the cooperative scale/bias blocks");
+    const int wave_lds = DMA ? DMA_WAVE_LDS : wave_lds_bytes(M, KPW, F::KBLK);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -179,6 +234,49 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             *reinterpret_cast<uint4*>(sblk + ((par * 2 + sc_arr) * 16 + sc_row) * sb_row + sc_cc * 16) = chunk;
     };
 
+    // Weight ring (DMA form): slot s of this wavefront holds its slice of one
+    // tile, 16 rows x RS bytes, as 16-byte pieces at position
+    // row * NP + (piece ^ swz(row)); the swizzle spreads the 16 rows that
+    // one fragment read touches over distinct banks.  Load instruction i
+    // fills positions 64 i .. 64 i + 63, lane q position 64 i + q, so each
+    // row's consecutive lanes read that row's slice -- whole lines.
+    constexpr int RS = KPW * F::KBLK * BITS / 8;  // bytes of a row in this wavefront's slice
+    constexpr int NP = RS / 16;                    // 16-byte pieces per row of the slice
+    constexpr int NI = DMA ? 16 * NP / 64 : 1;     // load instructions per slot
+    constexpr int SLOT = dma_slot_bytes<DT, BITS, GS, KPW>();
+    static_assert(!DMA || (NP >= 4 && 16 * NP % 64 == 0 && F::SEG * BITS / 8 == 16),
+                  "a slot is whole load instructions; a lane's segment is one piece");
+    auto swz = [](int row) { return ((row * NP) >> 4) & (NP - 1); };
+    const int64_t sb_blk = dma_sb_block_bytes(G);
+    const int PR = static_cast<int>(G / 8);  // 16-byte pieces per scale row
+    auto sb_swz = [PR](int row) { return ((row * PR) >> 4) & (PR - 1); };
+    uint8_t* const ring = lds + static_cast<int64_t>(W) * wave_lds +
+                          (DMA ? (DMA_SLOTS + 1) * sb_blk : COOP ? sb_lds_bytes(G) : 0) +
+                          static_cast<int64_t>(wave) * DMA_SLOTS * SLOT;
+    // DMA addressing: per lane a 32-bit byte offset fixed for the kernel, per
+    // tile a uniform base (scalar registers).  (These kernels run only when N
+    // spans many tiles, so a tile's 16 rows never pass N.)
+    uint32_t dma_off[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int p = 64 * i + lane;
+        const int row = p / NP, piece = (p % NP) ^ swz(p / NP);
+        dma_off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(row_bytes) +
+                     static_cast<uint32_t>(kb0 * F::KBLK * BITS / 8 + piece * 16);
+    }
+    // this wavefront's chunks all lie in one array (2G / sc_cpw = W / 2
+    // wavefronts per array): scales for the first half, biases for the rest
+    const uint8_t* const sb_arr = reinterpret_cast<const uint8_t*>(wave < W / 2 ? scales : biases);
+    const uint32_t ch_off = static_cast<uint32_t>(sc_row * 2 * G + (sc_cc ^ sb_swz(sc_row)) * 16);
+    // LDS byte addresses (M0) of this wavefront's slot 0 and of its chunk
+    // position in block 0
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds))));
+    const uint32_t m0_ring = lds0 + __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ring - lds));
+    const uint32_t m0_sb = lds0 + __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sblk - lds + 16 * wave * sc_cpw));
+    const int nfull = static_cast<int>(N / 16);     // tiles that end at or before column N
+    const int lastc = static_cast<int>(N - 16);    // first column of the shifted last tile
+
     // coop: the scale/bias chunk first (so that waiting for it does not wait
     // for the weights), else per-lane scale/bias words after the weights
     auto load_chunk = [&](int64_t tile, uint4& dst) __attribute__((always_inline)) {
@@ -188,7 +286,18 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             dst = *reinterpret_cast<const uint4*>(sc_src + srow * G + sc_cc * 8);
         }
     };
-    auto load_tile = [&](int64_t tile, Regs& r, auto coop_tag) __attribute__((always_inline)) {
+    // DMA form: 1 + NI load instructions per tile, in this order: this
+    // wavefront's chunks of the scale/bias block (position sc_q of block
+    // `blk`), then its weight slice (slot `slot`)
+    auto dma_col0 = [&](int tile) -> int { return tile < nfull ? tile * 16 : lastc; };
+    auto dma_tile = [&](int tile, int slot, int blk) __attribute__((always_inline)) {
+        const int64_t col0 = dma_col0(tile);
+        if (sc_on) dma16(sb_arr + col0 * G * 2, ch_off, m0_sb + static_cast<uint32_t>(blk * sb_blk));
+        const uint8_t* wt = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma16(wt, dma_off[i], m0_ring + static_cast<uint32_t>(slot * SLOT + 1024 * i));
+    };
+    auto load_tile = [&](int64_t tile, Regs& r, int slot, auto coop_tag) __attribute__((always_inline)) {
         constexpr bool coop = decltype(coop_tag)::value;
         const int64_t col0 = tile_col0(tile);
         if constexpr (coop && LA == 2) load_chunk(tile, r.sch);
@@ -232,14 +341,37 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const int64_t step = gridDim.x;
     auto body = [&](auto coop_tag) __attribute__((always_inline)) {
         constexpr bool coop = decltype(coop_tag)::value;
-        // ---- prologue.  This wavefront's activation rows [0, M) x its part of
-        // K are read with coalesced 16-byte loads (whole lines, every lane busy)
-        // ahead of the first tile's weights, then staged through its own LDS
-        // region and read back in fragment order.  Positions >= K are zero.
-        constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
-        constexpr int XG = (16 * CPR + 63) / 64;
-        uint4 xg[XG];
-        {
+        Regs buf[LA + 1];
+        int64_t tile = blockIdx.x;
+        uint4 xraw[KPW][F::STEPS];
+        if constexpr (DMA) {
+            // ---- prologue (weight ring).  The first DMA_SLOTS tiles go to
+            // slots (and blocks) 0, 1, ..., then the activations are read
+            // straight in fragment order (once per kernel, from L2 after the
+            // first workgroups).  Past the workgroup's last tile, loads
+            // re-read its first one.
+    #pragma unroll
+            for (int a = 0; a < DMA_SLOTS; ++a) {
+                const int t0 = static_cast<int>(blockIdx.x), ta = t0 + a * static_cast<int>(gridDim.x);
+                dma_tile(ta < static_cast<int>(ntiles) ? ta : t0, a, a);
+            }
+    #pragma unroll
+            for (int i = 0; i < KPW; ++i)
+    #pragma unroll
+                for (int s = 0; s < F::STEPS; ++s) {
+                    const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
+                    xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
+                    if (c < M)
+                        xraw[i][s] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * K + kb0 * F::KBLK + kk);
+                }
+        } else {
+            // ---- prologue.  This wavefront's activation rows [0, M) x its part of
+            // K are read with coalesced 16-byte loads (whole lines, every lane busy)
+            // ahead of the first tile's weights, then staged through its own LDS
+            // region and read back in fragment order.  Positions >= K are zero.
+            constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
+            constexpr int XG = (16 * CPR + 63) / 64;
+            uint4 xg[XG];
     #pragma unroll
             for (int j = 0; j < XG; ++j) {
                 const int t = lane + 64 * j;
@@ -248,28 +380,25 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 xg[j] = make_uint4(0u, 0u, 0u, 0u);
                 if (row < M && (VEC || k < K)) xg[j] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(row) * K + k);
             }
-        }
-        Regs buf[LA + 1];
-        int64_t tile = blockIdx.x;
-        load_tile(tile, buf[0], coop_tag);
-        __builtin_amdgcn_sched_barrier(0);
+            load_tile(tile, buf[0], 0, coop_tag);
+            __builtin_amdgcn_sched_barrier(0);
 
-        uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
+            uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
     #pragma unroll
-        for (int j = 0; j < XG; ++j) {
-            const int t = lane + 64 * j;
-            const int row = t / CPR, piece = t % CPR;
-            if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
-        }
-        uint4 xraw[KPW][F::STEPS];
-    #pragma unroll
-        for (int i = 0; i < KPW; ++i)
-    #pragma unroll
-            for (int s = 0; s < F::STEPS; ++s) {
-                const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-                xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
-                if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
+            for (int j = 0; j < XG; ++j) {
+                const int t = lane + 64 * j;
+                const int row = t / CPR, piece = t % CPR;
+                if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
             }
+    #pragma unroll
+            for (int i = 0; i < KPW; ++i)
+    #pragma unroll
+                for (int s = 0; s < F::STEPS; ++s) {
+                    const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
+                    xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
+                    if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
+                }
+        }
 
         Frag xa[KPW][F::STEPS];
     #pragma unroll
@@ -364,9 +493,9 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         };
 
         int parity = 0;
-        auto compute_store = [&](int64_t t, Regs& r, uint4 next_chunk, auto coop_tag) __attribute__((always_inline)) {
+        auto compute_store = [&](int64_t col0, Regs& r, int slot, uint4 next_chunk, auto coop_tag) __attribute__((always_inline)) {
             constexpr bool coop = decltype(coop_tag)::value;
-            if constexpr (coop) {
+            if constexpr (coop && !DMA) {
                 // this wavefront's scales and biases of tile t, from the block in LDS
                 r.sb.from_lds(sblk + (parity * 2 * 16 + c) * sb_row + (kb0 * F::KBLK / GS) * 2, 16 * sb_row);
             }
@@ -393,7 +522,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // the next tile's scale/bias block to the other parity; the barrier
             // below publishes it.  That buffer was last read in the previous
             // tile, before the previous barrier.
-            if constexpr (coop) stage_scales(next_chunk, parity ^ 1);
+            if constexpr (coop && !DMA) stage_scales(next_chunk, parity ^ 1);
             // Combine the wavefronts' partial sums: every wavefront writes its
             // partial to the buffer of this tile's parity at the start of its own
             // LDS region (over its staged activations, which it has read by then;
@@ -406,13 +535,21 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 256;
     #pragma unroll
             for (int q = 0; q < 4; ++q) rb[q * 64 + lane] = yacc[q];
+            if constexpr (DMA) {
+                // (after the partial's stores, so after the compute) this
+                // wavefront's chunks of the next tile's block have landed: after
+                // them come its weight slice and the DMA_SLOTS - 1 tiles after,
+                // NI + (DMA_SLOTS - 1) (1 + NI) loads.  The barrier publishes
+                // the block.
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI + (DMA_SLOTS - 1) * (1 + NI)) : "memory");
+            }
             __syncthreads();
             if (wave < 4) {
                 const int q = wave;
                 float v = 0.0f;
     #pragma unroll
                 for (int w = 0; w < W; ++w) v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 256 + q * 64 + lane];
-                const int64_t col = tile_col0(t) + c;
+                const int64_t col = col0 + c;
                 const int row = 4 * jj + q;
                 if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
             }
@@ -420,7 +557,54 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         };
 
         if constexpr (!MULTI) {  // a single tile: nothing to prefetch
-            compute_store(tile, buf[0], buf[0].sch, coop_tag);
+            compute_store(tile_col0(tile), buf[0], 0, buf[0].sch, coop_tag);
+            return;
+        }
+        if constexpr (DMA) {
+            // the first tiles have landed (the activation reads above were
+            // waited for, and they were issued last); publish their blocks
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            static_assert((DMA_SLOTS & (DMA_SLOTS + 1)) == 0, "DMA_SLOTS + 1 blocks: a power of two");
+            const int nt = static_cast<int>(ntiles), stp = static_cast<int>(gridDim.x);
+            int t = static_cast<int>(blockIdx.x);
+            int blk = 0;  // scale/bias block of the current tile
+            while (t < nt) {
+    #pragma unroll
+                for (int u = 0; u < DMA_SLOTS; ++u) {
+                    // Tile t (slot u) has landed once every load but those of
+                    // the DMA_SLOTS - 1 tiles after it has retired (the counter
+                    // retires loads in order; the compiler does not track these,
+                    // hence the explicit waits, which also keep the LDS reads
+                    // below from moving above them).
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DMA_SLOTS - 1) * (1 + NI)) : "memory");
+                    Regs& r = buf[0];
+                    const uint8_t* sl = ring + u * SLOT;
+    #pragma unroll
+                    for (int i = 0; i < KPW; ++i) {
+                        const int piece = (i * F::KBLK + jj * F::SEG) * BITS / 128;
+                        const uint4 v = *reinterpret_cast<const uint4*>(sl + 16 * (c * NP + (piece ^ swz(c))));
+                        r.w[i][0] = v.x; r.w[i][1] = v.y; r.w[i][2] = v.z; r.w[i][3] = v.w;
+                    }
+                    // this wavefront's NG scales and biases of tile t (2 NG bytes
+                    // inside one piece of row c)
+                    static_assert(2 * NG <= 16, "a wavefront's groups lie in one piece");
+                    const int gb = static_cast<int>(kb0 * F::KBLK / GS) * 2;  // byte offset in the row
+                    r.sb.from_lds(sblk + blk * sb_blk + c * 2 * G + ((gb >> 4) ^ sb_swz(c)) * 16 + (gb & 15), 32 * G);
+                    // the slot is refilled only after its reads have completed
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    const int next = t + DMA_SLOTS * stp;
+                    dma_tile(next < nt ? next : t, u, (blk + DMA_SLOTS) & DMA_SLOTS);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_store(dma_col0(t), r, u, r.sch, coop_tag);
+                    blk = (blk + 1) & DMA_SLOTS;
+                    t += stp;
+                    if (t >= nt) break;
+                }
+            }
+            // no global-to-LDS load may still be in flight when the
+            // workgroup's LDS is released
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             return;
         }
         // the tiles after the first up to the prefetch distance (buf[0] holds
@@ -428,7 +612,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     #pragma unroll
         for (int a = 1; a < LA; ++a) {
             const int64_t t_a = tile + a * step;
-            load_tile(t_a < ntiles ? t_a : tile, buf[a], coop_tag);
+            load_tile(t_a < ntiles ? t_a : tile, buf[a], a, coop_tag);
         }
         // distance 1: the chunks of the first two tiles (then two ahead)
         uint4 sch2[2];
@@ -453,11 +637,11 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     const int64_t next2 = tile + 2 * step;
                     load_chunk(next2 < ntiles ? next2 : tile, sch2[u]);
                 }
-                load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)], coop_tag);
+                load_tile(next < ntiles ? next : tile, buf[(u + LA) % (LA + 1)], (u + LA) % (LA + 1), coop_tag);
                 // keep the prefetch ahead of the compute: left alone, the
                 // scheduler sinks these loads past it to shorten live ranges
                 __builtin_amdgcn_sched_barrier(0);
-                compute_store(tile, buf[u], LA == 2 ? buf[(u + 1) % (LA + 1)].sch : sch2[(u + 1) % 2], coop_tag);
+                compute_store(tile_col0(tile), buf[u], u, LA == 2 ? buf[(u + 1) % (LA + 1)].sch : sch2[(u + 1) % 2], coop_tag);
                 tile += step;
                 if (tile >= ntiles) break;
             }
@@ -530,8 +714,14 @@ template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI>
 hipError_t launch_shape_m(const MatmulArgs& a) {
     const int64_t ntiles = (a.N + 15) / 16;
     const int64_t grid = reg_grid(ntiles, W);
-    const size_t lds = static_cast<size_t>(W) * wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK) +
-                       (MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(a.K / GS)) : 0);
+    constexpr bool dma = reg_dma<DT, BITS, GS, KPW, VEC, MULTI>();
+    const size_t wave_lds = dma ? DMA_WAVE_LDS : wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK);
+    const size_t lds = static_cast<size_t>(W) * wave_lds +
+                       (dma ? static_cast<size_t>(DMA_SLOTS + 1) * static_cast<size_t>(dma_sb_block_bytes(a.K / GS))
+                        : MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(a.K / GS))
+                                                                       : 0) +
+                       (dma ? static_cast<size_t>(W) * DMA_SLOTS * dma_slot_bytes<DT, BITS, GS, KPW>() : 0);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
         static const hipError_t attr = hipFuncSetAttribute(
