@@ -290,12 +290,26 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     // wavefront's chunks of the scale/bias block (position sc_q of block
     // `blk`), then its weight slice (slot `slot`)
     auto dma_col0 = [&](int tile) -> int { return tile < nfull ? tile * 16 : lastc; };
+    // Past the workgroup's last tile the ring still issues its loads (the
+    // waits count them), from the first KiB of x instead: L2-resident, and
+    // x holds at least M * K * 2 >= 1 KiB here.  Those slots are never read.
+    const uint32_t dummy_off = static_cast<uint32_t>(lane) * 16;
+    // (two branches on a uniform condition, not selects: a select between
+    // the offsets makes the compiler index a stack copy of dma_off)
     auto dma_tile = [&](int tile, int slot, int blk) __attribute__((always_inline)) {
-        const int64_t col0 = dma_col0(tile);
-        if (sc_on) dma16(sb_arr + col0 * G * 2, ch_off, m0_sb + static_cast<uint32_t>(blk * sb_blk));
-        const uint8_t* wt = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
+        const uint32_t m0w = m0_ring + static_cast<uint32_t>(slot * SLOT);
+        const uint32_t m0s = m0_sb + static_cast<uint32_t>(blk * sb_blk);
+        if (tile < static_cast<int>(ntiles)) {
+            const int64_t col0 = dma_col0(tile);
+            if (sc_on) dma16(sb_arr + col0 * G * 2, ch_off, m0s);
+            const uint8_t* wt = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dma16(wt, dma_off[i], m0_ring + static_cast<uint32_t>(slot * SLOT + 1024 * i));
+            for (int i = 0; i < NI; ++i) dma16(wt, dma_off[i], m0w + 1024 * i);
+        } else {
+            if (sc_on) dma16(x, dummy_off, m0s);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) dma16(x, dummy_off, m0w + 1024 * i);
+        }
     };
     auto load_tile = [&](int64_t tile, Regs& r, int slot, auto coop_tag) __attribute__((always_inline)) {
         constexpr bool coop = decltype(coop_tag)::value;
@@ -348,13 +362,10 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // ---- prologue (weight ring).  The first DMA_SLOTS tiles go to
             // slots (and blocks) 0, 1, ..., then the activations are read
             // straight in fragment order (once per kernel, from L2 after the
-            // first workgroups).  Past the workgroup's last tile, loads
-            // re-read its first one.
+            // first workgroups).
     #pragma unroll
-            for (int a = 0; a < DMA_SLOTS; ++a) {
-                const int t0 = static_cast<int>(blockIdx.x), ta = t0 + a * static_cast<int>(gridDim.x);
-                dma_tile(ta < static_cast<int>(ntiles) ? ta : t0, a, a);
-            }
+            for (int a = 0; a < DMA_SLOTS; ++a)
+                dma_tile(static_cast<int>(blockIdx.x) + a * static_cast<int>(gridDim.x), a, a);
     #pragma unroll
             for (int i = 0; i < KPW; ++i)
     #pragma unroll
@@ -593,8 +604,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     r.sb.from_lds(sblk + blk * sb_blk + c * 2 * G + ((gb >> 4) ^ sb_swz(c)) * 16 + (gb & 15), 32 * G);
                     // the slot is refilled only after its reads have completed
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    const int next = t + DMA_SLOTS * stp;
-                    dma_tile(next < nt ? next : t, u, (blk + DMA_SLOTS) & DMA_SLOTS);
+                    dma_tile(t + DMA_SLOTS * stp, u, (blk + DMA_SLOTS) & DMA_SLOTS);
                     __builtin_amdgcn_sched_barrier(0);
                     compute_store(dma_col0(t), r, u, r.sch, coop_tag);
                     blk = (blk + 1) & DMA_SLOTS;
