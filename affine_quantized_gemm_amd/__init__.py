@@ -57,7 +57,7 @@ def _load():
         "qmm_packed_words": (i64, [i32, i64]),
         "qmm_strerror": (ctypes.c_char_p, [i32]),
         "qmm_kernel_name": (ctypes.c_char_p, [i32]),
-        "qmm_probe_stream_read": (i32, [vp, i64, vp, i32, vp]),
+        "qmm_probe_stream_read": (i32, [vp, i64, vp, i32, i32, vp]),
         "qmm_probe_copy": (i32, [vp, vp, i64, vp]),
         "qmm_small_m_ws": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
         "qmm_small_m_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
@@ -164,13 +164,14 @@ def dequantize(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bit
     return out
 
 
-def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int = 0, stream=None):
-    """Stream ``src`` (whole tensor) through a read-only kernel (measurement helper)."""
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int = 0, shape: int = 1, stream=None):
+    """Stream ``src`` (whole tensor) through a read-only kernel (measurement
+    helper); shape 0: grid-stride loop, 1: 8 KiB chunks per wavefront."""
     _dev(src, "src")
     _dev(sink, "sink")
     if sink.numel() * sink.element_size() < 1024:
         raise ValueError("sink must hold 256 uint32")
-    _check(qmm_probe_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), grid,
+    _check(qmm_probe_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), grid, shape,
                                  _stream(stream)), "qmm_probe_stream_read")
 
 

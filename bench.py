@@ -274,11 +274,11 @@ def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
     views = [pool[i * B16:(i + 1) * B16] for i in range(n)]
     passes = max(1, -(-32 // n))  # at least 32 launches per replayed graph
     best = None
-    for grid in (1024, 2048, 4096):
-        def reads(grid=grid):
+    for shape, grid in ((0, 1024), (0, 2048), (0, 4096), (1, 256), (1, 512), (1, 1024)):
+        def reads(grid=grid, shape=shape):
             for _ in range(passes):
                 for v in views:
-                    Q.probe_stream_read(v, sink, grid)
+                    Q.probe_stream_read(v, sink, grid, shape)
         g = capture(torch, reads)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -288,9 +288,10 @@ def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * n * passes)
         if best is None or us < best[0]:
-            best = (us, grid)
+            best = (us, grid, shape)
     del pool
-    return {"us_per_call": round(best[0], 3), "gbs": round(B16 / (best[0] * 1e-6) / 1e9, 1), "grid": best[1]}
+    return {"us_per_call": round(best[0], 3), "gbs": round(B16 / (best[0] * 1e-6) / 1e9, 1), "grid": best[1],
+            "shape": best[2]}
 
 
 def copy_calibration(torch, Q):

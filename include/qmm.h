@@ -187,8 +187,12 @@ const char* qmm_kernel_name(int kernel_id);
  * Measurement helpers (not part of the matmul path).
  *
  * qmm_probe_stream_read: read `bytes` (a multiple of 16) from device memory
- * `src` with coalesced 16-byte nontemporal loads, `grid` workgroups of 256
- * threads (0 = 2048; never more than the data needs), and discard the data.
+ * `src` with coalesced 16-byte nontemporal loads and discard the data, in
+ * one of two shapes: `shape` 0, a grid-stride loop over `grid` workgroups of
+ * 256 threads (0 = 2048), four loads in flight per thread; `shape` 1, each
+ * wavefront reading whole 8 KiB chunks (8 loads of 1 KiB in flight) in
+ * `grid` workgroups of 1024 threads (0 = 512).  Never more workgroups than
+ * the data needs; another shape -> QMM_ERR_INVALID_ARG.
  * `sink` is caller-owned device memory of at least 256 uint32 that the
  * kernel may write (practically never does).  It is the streaming-read
  * ceiling a matmul streaming the same bytes can approach.
@@ -201,7 +205,7 @@ const char* qmm_kernel_name(int kernel_id);
  * sizes -> QMM_ERR_INVALID_ARG, other sizes -> QMM_ERR_UNSUPPORTED, 0 bytes
  * -> QMM_OK with nothing launched; asynchronous on `stream` like the rest.
  */
-int qmm_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, void* stream);
+int qmm_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, int shape, void* stream);
 int qmm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus

@@ -132,13 +132,15 @@ def test_select_kernel_is_total_over_supported_shapes():
 
 
 def test_probe_validation():
-    assert Q.qmm_probe_stream_read(A, -16, A, 0, None) == Q.QMM_ERR_INVALID_ARG
-    assert Q.qmm_probe_stream_read(A, 24, A, 0, None) == Q.QMM_ERR_UNSUPPORTED
-    assert Q.qmm_probe_stream_read(None, 64, A, 0, None) == Q.QMM_ERR_INVALID_ARG
-    assert Q.qmm_probe_stream_read(A, 64, None, 0, None) == Q.QMM_ERR_INVALID_ARG
-    assert Q.qmm_probe_stream_read(MIS, 64, A, 0, None) == Q.QMM_ERR_MISALIGNED
-    assert Q.qmm_probe_stream_read(A, 64, A, -1, None) == Q.QMM_ERR_INVALID_ARG
-    assert Q.qmm_probe_stream_read(None, 0, None, 0, None) == Q.QMM_OK
+    assert Q.qmm_probe_stream_read(A, -16, A, 0, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(A, 24, A, 0, 1, None) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_probe_stream_read(None, 64, A, 0, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(A, 64, None, 0, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(MIS, 64, A, 0, 1, None) == Q.QMM_ERR_MISALIGNED
+    assert Q.qmm_probe_stream_read(A, 64, A, -1, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(None, 0, None, 0, 1, None) == Q.QMM_OK
+    assert Q.qmm_probe_stream_read(A, 64, A, 0, 2, None) == Q.QMM_ERR_INVALID_ARG
+    assert Q.qmm_probe_stream_read(A, 64, A, 0, -1, None) == Q.QMM_ERR_INVALID_ARG
     assert Q.qmm_probe_copy(A, A, 8, None) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_probe_copy(A, MIS, 64, None) == Q.QMM_ERR_MISALIGNED
     assert Q.qmm_probe_copy(A, None, 64, None) == Q.QMM_ERR_INVALID_ARG

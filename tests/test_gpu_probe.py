@@ -26,11 +26,12 @@ def test_copy_exact(Q, nbytes):
     assert torch.equal(src, dst)
 
 
+@pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("nbytes,grid", [(16, 0), (4096 + 48, 0), ((8 << 20) + 16 * 7, 1024), (64 << 20, 4096)])
-def test_stream_read_runs(Q, nbytes, grid):
+def test_stream_read_runs(Q, nbytes, grid, shape):
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
-    Q.probe_stream_read(src, sink, grid)
+    Q.probe_stream_read(src, sink, grid, shape)
     torch.cuda.synchronize()
     # all-ones data XOR-reduces to a value that is never the kernel's trigger
     assert int(sink.abs().sum()) == 0
