@@ -115,23 +115,31 @@ __host__ __device__ inline int64_t sb_lds_bytes(int64_t G) { return 4 * 16 * sb_
 // consecutive lanes -- and half-line requests cap a long stream near 5.7 TB/s
 // on MI355X against 6.7-6.9 TB/s for whole 128-byte lines.  Here each
 // wavefront brings its slice in with direct global-to-LDS loads whose
-// consecutive lanes cover whole lines, into a ring of DMA_SLOTS slots of its
-// own, and reads its fragments from there; the prefetch ring then costs LDS
-// instead of registers.  A tile's slot is read into registers before the
-// slot is refilled, so DMA_SLOTS tiles are in flight during the compute.
+// consecutive lanes cover whole lines, into a ring of slots of its own, and
+// reads its fragments from there; the prefetch ring then costs LDS instead
+// of registers.  A tile's slot is read into registers before the slot is
+// refilled, so as many tiles as slots are in flight during the compute.
 // Activations are read in fragment order once per kernel (no staging area).
-template <int DT, int BITS, int GS, int KPW, bool VEC, bool MULTI>
+//
+// 4-bit: 3 slots of 16 rows x RS bytes (2 KiB at K = 4096).  8-bit: a slot
+// is 4 KiB at K = 4096, so 2 slots, and the partial-tile buffers keep only
+// rows 0..7 (M <= 8, a separate instantiation, MH) to fit 160 KiB of LDS.
+template <int DT, int BITS, int GS, int KPW, bool VEC, bool MULTI, bool MH>
 __host__ __device__ constexpr bool reg_dma() {
-    return MULTI && VEC && BITS == 4;
+    return MULTI && VEC && (BITS == 4 || (BITS == 8 && MH));
 }
+template <int BITS>
+__host__ __device__ constexpr int dma_slots() {
+    return BITS == 4 ? 3 : 2;
+}
+// per wavefront: the two partial-tile buffers (all 16 rows, or rows 0..7)
+__host__ __device__ constexpr int dma_wave_lds(bool mh) { return mh ? 1024 : 2048; }
 // bytes of one slot: 16 rows x the wavefront's KPW k-blocks
 template <int DT, int BITS, int GS, int KPW>
 __host__ __device__ constexpr int dma_slot_bytes() {
     return 16 * KPW * Fmt<DT, BITS, GS>::KBLK * BITS / 8;
 }
-constexpr int DMA_WAVE_LDS = 2048;  // per wavefront: the two partial-tile buffers
-constexpr int DMA_SLOTS = 3;        // weight slots per wavefront (tiles in flight)
-// Scale/bias blocks of the DMA form, DMA_SLOTS + 1 of them (a block is read
+// Scale/bias blocks of the DMA form, one more than the slots (a block is read
 // by every wavefront, so it is refilled only after the next barrier): the
 // tile's 16 rows of scales then of biases, rows of 2G bytes (unpadded) whose
 // 16-byte pieces are swizzled like the weight slots.
@@ -175,7 +183,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // they re-read its current tile, which was just fetched) and pinned ahead of
 // the compute, and nothing on the weight side is masked: positions beyond K
 // read valid addresses and meet zero activations.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI>
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
@@ -189,9 +197,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     using Regs = TileRegs<VEC, NGW, KPW, F::SEG_WORDS, F::PORTIONS>;
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int XS_ROW = xs_row_elems(KPW, F::KBLK);
-    constexpr bool DMA = reg_dma<DT, BITS, GS, KPW, VEC, MULTI>();
+    constexpr bool DMA = reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>();
+    constexpr int DMA_SLOTS = dma_slots<BITS>();
+    // partial-tile buffers: lanes stored per row quarter (rows 0..7 only: 32)
+    constexpr int PL = DMA && MH ? 32 : 64;
     static_assert(!DMA || COOP, "the weight ring carries the cooperative scale/bias blocks");
-    const int wave_lds = DMA ? DMA_WAVE_LDS : wave_lds_bytes(M, KPW, F::KBLK);
+    const int wave_lds = DMA ? dma_wave_lds(MH) : wave_lds_bytes(M, KPW, F::KBLK);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -543,9 +554,11 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // write this one after passing the next barrier, which the reducing
             // wavefronts reach only after reading.  Cooperative scale/bias blocks
             // follow the same parity.
-            float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 256;
+            float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 4 * PL;
+            if (lane < PL) {
     #pragma unroll
-            for (int q = 0; q < 4; ++q) rb[q * 64 + lane] = yacc[q];
+                for (int q = 0; q < 4; ++q) rb[q * PL + lane] = yacc[q];
+            }
             if constexpr (DMA) {
                 // (after the partial's stores, so after the compute) this
                 // wavefront's chunks of the next tile's block have landed: after
@@ -555,11 +568,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI + (DMA_SLOTS - 1) * (1 + NI)) : "memory");
             }
             __syncthreads();
-            if (wave < 4) {
+            if (wave < 4 && lane < PL) {
                 const int q = wave;
                 float v = 0.0f;
     #pragma unroll
-                for (int w = 0; w < W; ++w) v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 256 + q * 64 + lane];
+                for (int w = 0; w < W; ++w)
+                    v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 4 * PL + q * PL + lane];
                 const int64_t col = col0 + c;
                 const int row = 4 * jj + q;
                 if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
@@ -576,7 +590,6 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // waited for, and they were issued last); publish their blocks
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            static_assert((DMA_SLOTS & (DMA_SLOTS + 1)) == 0, "DMA_SLOTS + 1 blocks: a power of two");
             const int nt = static_cast<int>(ntiles), stp = static_cast<int>(gridDim.x);
             int t = static_cast<int>(blockIdx.x);
             int blk = 0;  // scale/bias block of the current tile
@@ -604,10 +617,10 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     r.sb.from_lds(sblk + blk * sb_blk + c * 2 * G + ((gb >> 4) ^ sb_swz(c)) * 16 + (gb & 15), 32 * G);
                     // the slot is refilled only after its reads have completed
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    dma_tile(t + DMA_SLOTS * stp, u, (blk + DMA_SLOTS) & DMA_SLOTS);
+                    dma_tile(t + DMA_SLOTS * stp, u, blk == 0 ? DMA_SLOTS : blk - 1);  // (blk + DMA_SLOTS) mod (DMA_SLOTS + 1)
                     __builtin_amdgcn_sched_barrier(0);
                     compute_store(dma_col0(t), r, u, r.sch, coop_tag);
-                    blk = (blk + 1) & DMA_SLOTS;
+                    blk = blk == DMA_SLOTS ? 0 : blk + 1;
                     t += stp;
                     if (t >= nt) break;
                 }
@@ -720,26 +733,34 @@ inline int64_t reg_grid(int64_t ntiles, int W) {
     return ntiles < resident ? ntiles : resident;
 }
 
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI>
+// dynamic LDS bytes of one workgroup
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
+size_t reg_lds_bytes(int64_t M, int64_t K) {
+    constexpr bool dma = reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>();
+    constexpr size_t DMA_SLOTS = static_cast<size_t>(dma_slots<BITS>());
+    const size_t wave_lds = dma ? dma_wave_lds(MH) : wave_lds_bytes(static_cast<int>(M), KPW, Fmt<DT, BITS, GS>::KBLK);
+    return static_cast<size_t>(W) * wave_lds +
+           (dma ? (DMA_SLOTS + 1) * static_cast<size_t>(dma_sb_block_bytes(K / GS))
+            : MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(K / GS))
+                                                           : 0) +
+           (dma ? static_cast<size_t>(W) * DMA_SLOTS * dma_slot_bytes<DT, BITS, GS, KPW>() : 0);
+}
+
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
 hipError_t launch_shape_m(const MatmulArgs& a) {
     const int64_t ntiles = (a.N + 15) / 16;
     const int64_t grid = reg_grid(ntiles, W);
-    constexpr bool dma = reg_dma<DT, BITS, GS, KPW, VEC, MULTI>();
-    const size_t wave_lds = dma ? DMA_WAVE_LDS : wave_lds_bytes(static_cast<int>(a.M), KPW, Fmt<DT, BITS, GS>::KBLK);
-    const size_t lds = static_cast<size_t>(W) * wave_lds +
-                       (dma ? static_cast<size_t>(DMA_SLOTS + 1) * static_cast<size_t>(dma_sb_block_bytes(a.K / GS))
-                        : MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(a.K / GS))
-                                                                       : 0) +
-                       (dma ? static_cast<size_t>(W) * DMA_SLOTS * dma_slot_bytes<DT, BITS, GS, KPW>() : 0);
+    if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
+    const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(a.M, a.K);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI>),
+            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH>), dim3(static_cast<unsigned>(grid)),
                        dim3(64 * W), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
                        static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
                        static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
@@ -749,8 +770,16 @@ hipError_t launch_shape_m(const MatmulArgs& a) {
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
 hipError_t launch_shape(const MatmulArgs& a) {
     const int64_t ntiles = (a.N + 15) / 16;
-    if (ntiles > reg_grid(ntiles, W)) return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true>(a);
-    return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false>(a);
+    if (ntiles > reg_grid(ntiles, W)) {
+        // 8-bit vector form at M <= 8: weights through LDS (partial tiles of
+        // rows 0..7) where that fits in LDS (not gs32 at K = 4096); otherwise
+        // the register-prefetch form
+        if constexpr (BITS == 8 && VEC)
+            if (a.M <= 8 && reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, true, true>(a.M, a.K) <= 160 * 1024)
+                return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, true>(a);
+        return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, false>(a);
+    }
+    return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false, false>(a);
 }
 
 template <int DT, int BITS, int GS>

@@ -221,21 +221,23 @@ def test_multi_tile_ragged(Q, dt, bits, gs):
     assert ok, worst
 
 
-@pytest.mark.parametrize("dt,gs,K", [("f16", 64, 4096), ("bf16", 32, 2048), ("bf16", 128, 4096)])
-def test_multi_tile_ring(Q, dt, gs, K):
-    """4-bit multi-tile kernel over 4-5 tiles per workgroup (1027 tiles of 16,
-    ragged last one), every output checked at M = 1, 4, 6, 16: the weight and
-    scale/bias ring wraps around more than once per workgroup."""
+@pytest.mark.parametrize("dt,bits,gs,K", [("f16", 4, 64, 4096), ("bf16", 4, 32, 2048), ("bf16", 4, 128, 4096),
+                                          ("f16", 8, 64, 4096), ("bf16", 8, 128, 4096), ("bf16", 8, 32, 4096)])
+def test_multi_tile_ring(Q, dt, bits, gs, K):
+    """Multi-tile kernel over 4-5 tiles per workgroup (1027 tiles of 16,
+    ragged last one), every output checked at M = 1, 4, 6, 8, 16: the weight
+    and scale/bias ring wraps around more than once per workgroup (4-bit;
+    8-bit at M <= 8 where its ring fits in LDS, the register form above)."""
     N = 16 * 1027 + 5
-    w = synth.normal((N, K), 0.02, dt, 7000 + gs)
-    owq, osc, obi = oracle_quant(w, dt, 4, gs)
+    w = synth.normal((N, K), 0.02, dt, 7000 + gs + bits)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
     wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
-    for M in (1, 4, 6, 16):
-        print(f"ring {dt} gs{gs} M={M} N={N} K={K}", flush=True)
+    for M in (1, 4, 6, 8, 16):
+        print(f"ring {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
         x = synth.normal((M, K), 1.0, dt, 7100 + M)
-        y = Q.small_m(x.cuda(), wq, sc, bi, 4, gs, kernel=Q.KERNEL_MFMA_REG)
+        y = Q.small_m(x.cuda(), wq, sc, bi, bits, gs, kernel=Q.KERNEL_MFMA_REG)
         torch.cuda.synchronize()
-        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, 4, gs)
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
         ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
         assert ok, (M, worst)
 
