@@ -370,21 +370,22 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         int64_t tile = blockIdx.x;
         uint4 xraw[KPW][F::STEPS];
         if constexpr (DMA) {
-            // ---- prologue (weight ring).  The first DMA_SLOTS tiles go to
-            // slots (and blocks) 0, 1, ..., then the activations are read
-            // straight in fragment order (once per kernel, from L2 after the
-            // first workgroups).
-    #pragma unroll
-            for (int a = 0; a < DMA_SLOTS; ++a)
-                dma_tile(static_cast<int>(blockIdx.x) + a * static_cast<int>(gridDim.x), a, a);
+            // ---- prologue (weight ring).  The first tile goes to slot (and
+            // block) 0, then the activations are read straight in fragment
+            // order (once per kernel, from L2 after the first workgroups).
+            // The next tiles are issued once the activations are in: the
+            // wait for them would otherwise also wait for those tiles.
+            dma_tile(static_cast<int>(blockIdx.x), 0, 0);
+            // every lane loads (rows past M re-read row M - 1 and are zeroed
+            // after the conversion below): a conditional load merged with a
+            // zero makes the compiler wait for it right away
+            const int64_t crow = c < M ? c : M - 1;
     #pragma unroll
             for (int i = 0; i < KPW; ++i)
     #pragma unroll
                 for (int s = 0; s < F::STEPS; ++s) {
                     const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-                    xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
-                    if (c < M)
-                        xraw[i][s] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * K + kb0 * F::KBLK + kk);
+                    xraw[i][s] = *reinterpret_cast<const uint4*>(x + crow * K + kb0 * F::KBLK + kk);
                 }
         } else {
             // ---- prologue.  This wavefront's activation rows [0, M) x its part of
@@ -426,7 +427,14 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     #pragma unroll
         for (int i = 0; i < KPW; ++i)
     #pragma unroll
-            for (int s = 0; s < F::STEPS; ++s) xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
+            for (int s = 0; s < F::STEPS; ++s) {
+                xa[i][s] = x_frag<BITS, DT>(xraw[i][s]);
+                if constexpr (DMA) {
+                    if (c >= M)
+    #pragma unroll
+                        for (int v = 0; v < 4; ++v) xa[i][s].v[v] = 0u;
+                }
+            }
 
         // Unit sums X_u = sum x and O_u = sum x*off of row c over each unit of
         // this wavefront, on the matrix cores: with B = the activation fragment
@@ -586,9 +594,15 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             return;
         }
         if constexpr (DMA) {
-            // the first tiles have landed (the activation reads above were
-            // waited for, and they were issued last); publish their blocks
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // tiles 1 .. DMA_SLOTS - 1 to their slots; then the first tile has
+            // landed once only their loads may be outstanding (the
+            // activations, issued after it, were already waited for), and
+            // the barrier publishes its scale/bias block.  Each later block
+            // is published by the loop, one tile ahead.
+    #pragma unroll
+            for (int a = 1; a < DMA_SLOTS; ++a)
+                dma_tile(static_cast<int>(blockIdx.x) + a * static_cast<int>(gridDim.x), a, a);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DMA_SLOTS - 1) * (1 + NI)) : "memory");
             __syncthreads();
             const int nt = static_cast<int>(ntiles), stp = static_cast<int>(gridDim.x);
             int t = static_cast<int>(blockIdx.x);
