@@ -139,12 +139,20 @@ int qmm_small_m_split_forced(int dt, int bits, int group_size, int64_t M, int64_
     int st = check_matmul(dt, bits, group_size, M, N, K, x, wq, scales, biases, y);
     if (st != QMM_OK) return st;
     if (split < 1 || workspace_bytes < 0) return QMM_ERR_INVALID_ARG;
-    if (!qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K)) return QMM_ERR_UNSUPPORTED;
     const int cfg = kernel_id == QMM_KERNEL_MFMA_TILE16  ? qmm::TILE_CFG_16
                     : kernel_id == QMM_KERNEL_MFMA_TILE64 ? qmm::TILE_CFG_64
                                                           : -1;
-    if (split > 1 && cfg < 0) return QMM_ERR_UNSUPPORTED;
-    const int eff = split > 1 ? qmm::tile_split(bits, K, cfg, split) : 1;
+    int eff = 1;
+    if (split > 1 && kernel_id == QMM_KERNEL_MFMA_REG) {
+        // the register kernel splits K into exactly `split` slices it covers
+        // (it cannot run K that deep split-free)
+        if (!qmm::mfma_reg_split_supports(bits, group_size, M, N, K, split)) return QMM_ERR_UNSUPPORTED;
+        eff = split;
+    } else {
+        if (!qmm::kernel_supports(kernel_id, dt, bits, group_size, M, N, K)) return QMM_ERR_UNSUPPORTED;
+        if (split > 1 && cfg < 0) return QMM_ERR_UNSUPPORTED;
+        eff = split > 1 ? qmm::tile_split(bits, K, cfg, split) : 1;
+    }
     if (M == 0 || N == 0) return QMM_OK;
     if (eff > 1) {
         if (workspace == nullptr || workspace_bytes < static_cast<int64_t>(eff) * M * N * 4)

@@ -35,6 +35,13 @@ hipError_t launch_mfma_pass(const MatmulArgs& a);
 enum { TILE_CFG_16 = 0, TILE_CFG_64 = 1 };
 hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg);
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K);
+// The register kernel's K split (4-bit LDS-ring form): K a whole number
+// `split` of slices that form covers, with more column tiles than
+// workgroups per slice.
+bool mfma_reg_split_supports(int bits, int gs, int64_t M, int64_t N, int64_t K, int split);
+// y[i] = sum over s < split of part[s * mn + i], in that order, rounded once
+// to dt (the second kernel of every K split).
+hipError_t launch_reduce_partials(int dt, const float* part, void* y, int split, int64_t mn, hipStream_t st);
 bool mfma_tile_supports(int bits, int64_t M, int64_t K, int cfg);
 // A split count made valid for the tile kernel (every split gets at least
 // one pass); the workspace holds that many partial outputs.

@@ -183,10 +183,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // they re-read its current tile, which was just fetched) and pinned ahead of
 // the compute, and nothing on the weight side is masked: positions beyond K
 // read valid addresses and meet zero activations.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
+//
+// K split (SPLIT, weights-through-LDS form only): slice blockIdx.y covers K
+// positions [s K, (s + 1) K) of rows ldk long, and the workgroup leaves an
+// fp32 partial output in part[s][M][N] instead of y; a second kernel adds
+// the slices in order.  Unsplit: ldk = K, part unused.
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K) {
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K, int64_t ldk,
+    float* __restrict__ part) {
     using F = Fmt<DT, BITS, GS>;
     constexpr int LA = reg_lead<DT, BITS, GS, KPW, VEC>();
     constexpr bool COOP = MULTI && reg_coop<DT, BITS, GS, KPW, VEC>();
@@ -208,8 +214,17 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15;   // tile column of this lane's B operand / D output, row of its A operand
     const int jj = lane >> 4;  // k-slot quarter
-    const int64_t row_words = K * BITS / 32;
-    const int64_t G = K / GS;
+    static_assert(!SPLIT || reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>(), "the K split runs the LDS-ring form");
+    if constexpr (SPLIT) {
+        const int64_t sk = static_cast<int64_t>(blockIdx.y) * K;
+        x += sk;
+        wq += sk * BITS / 32;
+        scales += sk / GS;
+        biases += sk / GS;
+    }
+    const int64_t row_words = ldk * BITS / 32;
+    const int64_t G = K / GS;     // groups of a row within the K range (the LDS block layout)
+    const int64_t Gf = ldk / GS;  // scale/bias row stride
     const int64_t ntiles = (N + 15) / 16;
     const int64_t kb0 = static_cast<int64_t>(wave) * KPW;
 
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     // this wavefront's chunks all lie in one array (2G / sc_cpw = W / 2
     // wavefronts per array): scales for the first half, biases for the rest
     const uint8_t* const sb_arr = reinterpret_cast<const uint8_t*>(wave < W / 2 ? scales : biases);
-    const uint32_t ch_off = static_cast<uint32_t>(sc_row * 2 * G + (sc_cc ^ sb_swz(sc_row)) * 16);
+    const uint32_t ch_off = static_cast<uint32_t>(sc_row * 2 * Gf + (sc_cc ^ sb_swz(sc_row)) * 16);
     // LDS byte addresses (M0) of this wavefront's slot 0 and of its chunk
     // position in block 0
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
@@ -303,7 +318,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     auto dma_col0 = [&](int tile) -> int { return tile < nfull ? tile * 16 : lastc; };
     // Past the workgroup's last tile the ring still issues its loads (the
     // waits count them), from the first KiB of x instead: L2-resident, and
-    // x holds at least M * K * 2 >= 1 KiB here.  Those slots are never read.
+    // K >= 512 here, so row 0 of x holds at least 1 KiB of this K range.
+    // Those slots are never read.
     const uint32_t dummy_off = static_cast<uint32_t>(lane) * 16;
     // (two branches on a uniform condition, not selects: a select between
     // the offsets makes the compiler index a stack copy of dma_off)
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         const uint32_t m0s = m0_sb + static_cast<uint32_t>(blk * sb_blk);
         if (tile < static_cast<int>(ntiles)) {
             const int64_t col0 = dma_col0(tile);
-            if (sc_on) dma16(sb_arr + col0 * G * 2, ch_off, m0s);
+            if (sc_on) dma16(sb_arr + col0 * Gf * 2, ch_off, m0s);
             const uint8_t* wt = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
             for (int i = 0; i < NI; ++i) dma16(wt, dma_off[i], m0w + 1024 * i);
@@ -385,7 +401,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     #pragma unroll
                 for (int s = 0; s < F::STEPS; ++s) {
                     const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-                    xraw[i][s] = *reinterpret_cast<const uint4*>(x + crow * K + kb0 * F::KBLK + kk);
+                    xraw[i][s] = *reinterpret_cast<const uint4*>(x + crow * ldk + kb0 * F::KBLK + kk);
                 }
         } else {
             // ---- prologue.  This wavefront's activation rows [0, M) x its part of
@@ -584,7 +600,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 4 * PL + q * PL + lane];
                 const int64_t col = col0 + c;
                 const int row = 4 * jj + q;
-                if (col < N && row < M) y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
+                if (col < N && row < M) {
+                    if constexpr (SPLIT)
+                        part[(static_cast<int64_t>(blockIdx.y) * M + row) * N + col] = v;
+                    else
+                        y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
+                }
             }
             parity ^= 1;
         };
@@ -760,25 +781,32 @@ size_t reg_lds_bytes(int64_t M, int64_t K) {
            (dma ? static_cast<size_t>(W) * DMA_SLOTS * dma_slot_bytes<DT, BITS, GS, KPW>() : 0);
 }
 
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
-hipError_t launch_shape_m(const MatmulArgs& a) {
+// Launch over K range kr of rows a.K long: kr = a.K unsplit, a.K / S split
+// S ways (grid.y = S, each slice with its share of the resident workgroups).
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT = false>
+hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
+    const int S = SPLIT ? a.split : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = reg_grid(ntiles, W);
+    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / S : reg_grid(ntiles, W);
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
-    const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(a.M, a.K);
+    if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
+    const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(a.M, kr);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH>),
+            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH>), dim3(static_cast<unsigned>(grid)),
-                       dim3(64 * W), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
-                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
-                       static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N, a.K);
-    return hipGetLastError();
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT>),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(S)), dim3(64 * W), lds, a.stream,
+                       static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
+                       static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
+                       kr, a.K, a.part);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if constexpr (SPLIT) return launch_reduce_partials(DT, a.part, a.y, S, a.M * a.N, a.stream);
+    return hipSuccess;
 }
 
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
@@ -790,15 +818,35 @@ hipError_t launch_shape(const MatmulArgs& a) {
         // the register-prefetch form
         if constexpr (BITS == 8 && VEC)
             if (a.M <= 8 && reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, true, true>(a.M, a.K) <= 160 * 1024)
-                return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, true>(a);
-        return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, false>(a);
+                return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, true>(a, a.K);
+        return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, false>(a, a.K);
     }
-    return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false, false>(a);
+    return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false, false>(a, a.K);
+}
+
+// K split: the LDS-ring form (4-bit, vector form, 16 wavefronts) on slices
+// of K / split, each slice with 256 / split workgroups walking more column
+// tiles than that.
+inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, int split, RegShape& s) {
+    if (bits != 4 || M > 16 || split < 2 || K % split != 0) return false;
+    if (!pick_shape(bits, gs, K / split, s) || !s.vec || s.W != 16) return false;
+    const int64_t ntiles = (N + 15) / 16;
+    const int64_t per_slice = reg_grid(ntiles, 16) / split;
+    return per_slice >= 1 && ntiles > per_slice;
 }
 
 template <int DT, int BITS, int GS>
 hipError_t launch_reg_t(const MatmulArgs& a) {
     RegShape s;
+    if (a.split > 1) {
+        if (!reg_split_shape(BITS, GS, a.M, a.N, a.K, a.split, s)) return hipErrorInvalidValue;
+        if constexpr (BITS == 4) {
+            const int64_t kr = a.K / a.split;
+            if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, true>(a, kr);
+            if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, true>(a, kr);
+        }
+        return hipErrorInvalidValue;
+    }
     if (!pick_shape(BITS, GS, a.K, s)) return hipErrorInvalidValue;
     switch (s.W * 100 + s.KPW * 2 + (s.vec ? 1 : 0)) {
         case 402: return launch_shape<DT, BITS, GS, 4, 1, false>(a);
@@ -825,6 +873,11 @@ bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K) {
     if (M > 16) return false;
     RegShape s;
     return pick_shape(bits, gs, K, s);
+}
+
+bool mfma_reg_split_supports(int bits, int gs, int64_t M, int64_t N, int64_t K, int split) {
+    RegShape s;
+    return reg_split_shape(bits, gs, M, N, K, split, s);
 }
 
 hipError_t launch_mfma_reg(const MatmulArgs& a) {

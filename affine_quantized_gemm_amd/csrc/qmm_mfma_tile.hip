@@ -447,10 +447,7 @@ hipError_t launch_tile_cfg(const MatmulArgs& a) {
                        S > 1 ? a.part : nullptr, static_cast<int>(a.M), a.N, a.K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    const int64_t mn = a.M * a.N;
-    hipLaunchKernelGGL((reduce_partials_kernel<DT>), dim3(static_cast<unsigned>((mn + 255) / 256)), dim3(256), 0,
-                       a.stream, a.part, static_cast<uint16_t*>(a.y), S, mn);
-    return hipGetLastError();
+    return launch_reduce_partials(DT, a.part, a.y, S, a.M * a.N, a.stream);
 }
 
 // Every shape runs 4 compute wavefronts and 2 loaders (6 wavefronts: at
@@ -469,6 +466,16 @@ hipError_t launch_tile_t(const MatmulArgs& a, int cfg) {
 }
 
 }  // namespace
+
+hipError_t launch_reduce_partials(int dt, const float* part, void* y, int split, int64_t mn, hipStream_t st) {
+    if (mn <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((mn + 255) / 256));
+    if (dt == 0)
+        hipLaunchKernelGGL((reduce_partials_kernel<0>), grid, dim3(256), 0, st, part, static_cast<uint16_t*>(y), split, mn);
+    else
+        hipLaunchKernelGGL((reduce_partials_kernel<1>), grid, dim3(256), 0, st, part, static_cast<uint16_t*>(y), split, mn);
+    return hipGetLastError();
+}
 
 int tile_split(int bits, int64_t K, int cfg, int split) {
     const int64_t kblk = bits == 4 ? 128 : 64;

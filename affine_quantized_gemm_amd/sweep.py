@@ -73,7 +73,9 @@ def time_calls(fn, n_calls, reps=5):
     return best
 
 
-SPLITS = ((3, 2), (3, 4), (4, 2), (4, 4), (4, 8))   # (tile kernel id, K split) timed with --splits
+# (kernel id, K split) timed with --splits: the tile kernels, and the
+# register kernel on K it takes only split (slices it covers whole)
+SPLITS = ((3, 2), (3, 4), (4, 2), (4, 4), (4, 8), (1, 2), (1, 4), (1, 7))
 
 
 def sweep_shape(name, ms, stack_mib, splits=False):
@@ -104,7 +106,9 @@ def sweep_shape(name, ms, stack_mib, splits=False):
         if splits:
             ws = torch.empty((64 * M * N * 4 + 16,), dtype=torch.uint8, device="cuda")
             for kid, sp in SPLITS:
-                if not Q.kernel_supported(tdt, bits, gs, M, N, K, kid):
+                try:  # one call decides whether this (kernel, split) runs the shape
+                    Q.small_m_ws(x, *stack[0], bits, gs, workspace=ws, out=y, kernel=kid, split=sp)
+                except Q.QmmError:
                     continue
 
                 def run_s(kid=kid, sp=sp):

@@ -177,8 +177,9 @@ def test_dispatch_follows_measured_crossovers():
 def test_split_plan_and_workspace_bytes():
     """The K-split plan of qmm_small_m_ws (crossovers measured with sweep.py
     --splits): the 64-column tile kernel split min(4, 256 / tiles) ways when N
-    gives 32..64 such tiles and M >= 24 (K >= 8192) or M >= 48; otherwise no
-    split and no workspace (exactly qmm_small_m)."""
+    gives 32..64 such tiles and M >= 24 (K >= 8192) or M >= 48; at M <= 16 the
+    register kernel on the fewest K slices it covers, where it cannot take K
+    whole; otherwise no split and no workspace (exactly qmm_small_m)."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
     # down projection 4096 x 14336: 64 tiles -> 4 splits of 28 passes (7 each), from M = 24
@@ -189,8 +190,13 @@ def test_split_plan_and_workspace_bytes():
     assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
     # N = 2048: 32 tiles -> 4 splits (capped)
     assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+    # M <= 16 on K the register kernel takes only split: 7 slices of 2048 (down), 2 of 4096 (K = 8192)
+    for M in (1, 8, 16):
+        assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_REG, 7)
+        assert Q.workspace_bytes(f16, 4, 64, M, 4096, 14336) == 7 * M * 4096 * 4
+    assert Q.split_plan(bf16, 4, 32, 8, 4096, 8192) == (Q.KERNEL_MFMA_REG, 2)
     # no split: small M, few tiles (k/v), many tiles (gate/up, LM head), K the tile kernels do not take
-    for args in ((f16, 4, 64, 16, 4096, 14336), (f16, 4, 64, 36, 4096, 4096), (f16, 4, 64, 64, 1024, 4096),
+    for args in ((f16, 8, 64, 16, 4096, 14336), (f16, 4, 64, 36, 4096, 4096), (f16, 4, 64, 64, 1024, 4096),
                  (f16, 4, 64, 64, 14336, 4096), (bf16, 4, 64, 64, 151936, 4096), (f16, 4, 64, 64, 4096, 14400),
                  (f16, 4, 64, 6, 4096, 4096)):
         k, s = Q.split_plan(*args)
@@ -214,6 +220,13 @@ def test_split_entry_validation():
     assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_TILE64, 0) == Q.QMM_ERR_INVALID_ARG
     assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_PASS, 2) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_REG, 1) == Q.QMM_ERR_UNSUPPORTED
+    # the register kernel splits K exactly: 14336 = 7 slices of 2048 (not 2 of 7168), M <= 16 only
+    small = (f16, 4, 64, 8, 4096, 14336, A, A, A, A, A)
+    assert Q.qmm_small_m_split_forced(*small, A, 7 * 8 * 4096 * 4, None, Q.KERNEL_MFMA_REG, 2) == \
+        Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_REG, 7) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_small_m_split_forced(*small, A, 7 * 8 * 4096 * 4 - 4, None, Q.KERNEL_MFMA_REG, 7) == \
+        Q.QMM_ERR_INVALID_ARG
     # the workspace a forced split needs is the reduced split's: 28 passes, split 5 -> 6 passes each -> 5 splits
     assert Q.qmm_small_m_split_forced(*base, A, 5 * 32 * 4096 * 4 - 4, None, Q.KERNEL_MFMA_TILE16, 5) == \
         Q.QMM_ERR_INVALID_ARG

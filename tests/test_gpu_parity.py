@@ -300,11 +300,35 @@ def test_split_k(Q, kernel, dt, bits, gs):
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (M, split)
 
 
-@pytest.mark.parametrize("M", [24, 36, 64])
+@pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
+                                             ("f16", 128, 8192, (2,))])
+def test_reg_split_k(Q, dt, gs, K, splits):
+    """The register kernel's K split (slices it covers, fp32 partials in the
+    workspace, fixed-order reduction) over a ragged N (258 tiles of 16), every
+    output checked; two runs bit-identical."""
+    N = 16 * 257 + 5
+    w = synth.normal((N, K), 0.02, dt, 8000 + gs)
+    owq, osc, obi = oracle_quant(w, dt, 4, gs)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    for M in (1, 8, 16):
+        x = synth.normal((M, K), 1.0, dt, 8100 + M)
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, 4, gs)
+        for split in splits:
+            print(f"reg split {dt} gs{gs} M={M} N={N} K={K} split={split}", flush=True)
+            y0 = Q.small_m_ws(x.cuda(), wq, sc, bi, 4, gs, kernel=Q.KERNEL_MFMA_REG, split=split)
+            y1 = Q.small_m_ws(x.cuda(), wq, sc, bi, 4, gs, kernel=Q.KERNEL_MFMA_REG, split=split)
+            torch.cuda.synchronize()
+            assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+            ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y0), dt), yo, T)
+            assert ok, (M, split, worst)
+
+
+@pytest.mark.parametrize("M", [8, 16, 24, 36, 64])
 def test_small_m_ws_planned(Q, M):
-    """qmm_small_m_ws with its own plan on the down projection (4096 x 14336,
-    split 4) against the oracle, and equal to qmm_small_m within tolerance of
-    the oracle too; a plan without a split takes no workspace."""
+    """qmm_small_m_ws with its own plan on the down projection (4096 x 14336:
+    the register kernel on 7 K slices at M <= 16, the 64-column tile kernel
+    split 4 ways above) against the oracle; a plan without a split takes no
+    workspace."""
     dt, bits, gs, N, K = "f16", 4, 64, 4096, 14336
     assert Q.split_plan(torch.float16, bits, gs, M, N, K)[1] > 1
     w = synth.normal((N, K), 0.02, dt, 900 + M)
