@@ -4,10 +4,10 @@
 
 namespace qmm {
 
-bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /*N*/, int64_t K) {
+bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     switch (kid) {
         case QMM_KERNEL_VALU: return M <= 64;
-        case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, gs, M, K);
+        case QMM_KERNEL_MFMA_REG: return mfma_reg_supports(bits, gs, M, N, K);
         case QMM_KERNEL_MFMA_PASS: return M <= 64;
         case QMM_KERNEL_MFMA_TILE16: return mfma_tile_supports(bits, M, K, TILE_CFG_16);
         case QMM_KERNEL_MFMA_TILE64: return mfma_tile_supports(bits, M, K, TILE_CFG_64);
@@ -22,7 +22,14 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /
 //     K = N = 4096, 4-bit; the pass kernel for longer K (18.4 us vs 25.2 us
 //     for the 16-column tile kernel at M = 8 on the 4096 x 14336 down
 //     projection);
-//   * M > 16, wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
+//   * M 17..64, 4-bit, K <= 4096, more 16-column tiles than the row-block
+//     grid's column slots: the register kernel on row blocks (one 16-row
+//     block per workgroup layer, weights shared through the XCD's L2):
+//     15.3 / 16.1 / 23.7 us vs 24.1 / 24.3 / 34.1 us (64-column tiles) at
+//     M = 24 / 32 / 64 on the 14336 x 4096 gate/up projection, 9.5 / 11.3 /
+//     11.9 us vs 12.9 (pass) / 16.0 / 20.6 (16-column tiles) at M = 24 / 36 /
+//     64, K = N = 4096, 99 / 188 us vs 190 / 287 us on the LM head;
+//   * otherwise, M > 16, wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
 //     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
 //     projection, 186 / 278 us vs 368 / 669 us on the 151936-column LM head;
 //   * M > 32, N from 4096 (at least one 16-column tile per CU): the
@@ -38,9 +45,8 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t /
 // The pages' own dispatch is likewise a measured crossover in M per shape
 // (MLX issue #4720, "Root cause"; crossover near M = 6-8 on Apple parts).
 int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
-    if (M <= 16)
-        return kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K) ? QMM_KERNEL_MFMA_REG
-                                                                           : QMM_KERNEL_MFMA_PASS;
+    if (kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K)) return QMM_KERNEL_MFMA_REG;
+    if (M <= 16) return QMM_KERNEL_MFMA_PASS;
     if (kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) {
         if (N >= 8192) return QMM_KERNEL_MFMA_TILE64;
         if (M > 32 && N >= 4096) return QMM_KERNEL_MFMA_TILE16;
@@ -64,7 +70,8 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 // 22.5 us for the split-free pass kernel at M = 1 / 8 / 16.
 SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     SplitPlan p{select_kernel(dt, bits, gs, M, N, K), 1};
-    if (M <= 16 && p.kernel != QMM_KERNEL_MFMA_REG) {
+    if (p.kernel == QMM_KERNEL_MFMA_REG) return p;  // faster than any split measured
+    if (M <= 16) {
         for (int s = 2; s <= 8; ++s)
             if (mfma_reg_split_supports(bits, gs, M, N, K, s)) return SplitPlan{QMM_KERNEL_MFMA_REG, s};
         return p;

@@ -156,6 +156,10 @@ __host__ __device__ inline int64_t dma_sb_block_bytes(int64_t G) { return 2 * 16
 // base: a 64-bit address, the same in every lane (moved to scalar
 // registers here); voff: this lane's byte offset from it; m0: the LDS byte
 // address of lane 0's 16 bytes (the same in every lane).
+//
+// NT: non-temporal (each weight line is read once).  Without it (row-block
+// grids) L2 keeps the line for the other row blocks of the same column slot.
+template <bool NT = true>
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0) {
     // (readfirstlane returns a signed int: each half goes through uint32_t so
     // that widening cannot sign-extend the low word over the high one)
@@ -163,10 +167,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
     const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(sb)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(sb)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(sb)
+                     : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -188,7 +198,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // positions [s K, (s + 1) K) of rows ldk long, and the workgroup leaves an
 // fp32 partial output in part[s][M][N] instead of y; a second kernel adds
 // the slices in order.  Unsplit: ldk = K, part unused.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT>
+//
+// Row blocks (ROWS, LDS-ring form, not with SPLIT): M up to 64, workgroup
+// (., ., z) computes rows [16 z, 16 z + 16) -- its own activation rows,
+// every column tile of its slot.  The row blocks of a column slot are
+// resident together on one XCD (linear workgroup ids congruent mod 8), so a
+// tile's weights come from HBM once and from that XCD's L2 for the others.
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K, int64_t ldk,
@@ -215,6 +231,14 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const int c = lane & 15;   // tile column of this lane's B operand / D output, row of its A operand
     const int jj = lane >> 4;  // k-slot quarter
     static_assert(!SPLIT || reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>(), "the K split runs the LDS-ring form");
+    static_assert(!ROWS || (reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() && !SPLIT && !MH),
+                  "row blocks run the LDS-ring form, unsplit, all 16 rows");
+    if constexpr (ROWS) {
+        const int r0 = 16 * static_cast<int>(blockIdx.z);
+        x += static_cast<int64_t>(r0) * ldk;
+        y += static_cast<int64_t>(r0) * N;
+        M = M - r0 < 16 ? M - r0 : 16;
+    }
     if constexpr (SPLIT) {
         const int64_t sk = static_cast<int64_t>(blockIdx.y) * K;
         x += sk;
@@ -328,10 +352,10 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         const uint32_t m0s = m0_sb + static_cast<uint32_t>(blk * sb_blk);
         if (tile < static_cast<int>(ntiles)) {
             const int64_t col0 = dma_col0(tile);
-            if (sc_on) dma16(sb_arr + col0 * Gf * 2, ch_off, m0s);
+            if (sc_on) dma16<!ROWS>(sb_arr + col0 * Gf * 2, ch_off, m0s);
             const uint8_t* wt = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) dma16(wt, dma_off[i], m0w + 1024 * i);
+            for (int i = 0; i < NI; ++i) dma16<!ROWS>(wt, dma_off[i], m0w + 1024 * i);
         } else {
             if (sc_on) dma16(x, dummy_off, m0s);
 #pragma unroll
@@ -767,6 +791,17 @@ inline int64_t reg_grid(int64_t ntiles, int W) {
     const int64_t resident = 256 * (16 / W);
     return ntiles < resident ? ntiles : resident;
 }
+// row-block grids: column slots per row block, a multiple of 8 so that the
+// row blocks of a slot (linear ids slot + k * slots) share an XCD
+inline int64_t reg_rows_grid(int rb) { return (256 / rb) / 8 * 8; }
+
+// Row blocks (M 17..64): the LDS-ring form (4-bit, vector form, 16
+// wavefronts) with more column tiles than slots.
+inline bool reg_rows_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, RegShape& s) {
+    if (bits != 4 || M <= 16 || M > 64) return false;
+    if (!pick_shape(bits, gs, K, s) || !s.vec || s.W != 16) return false;
+    return (N + 15) / 16 > reg_rows_grid(static_cast<int>((M + 15) / 16));
+}
 
 // dynamic LDS bytes of one workgroup
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
@@ -783,11 +818,14 @@ size_t reg_lds_bytes(int64_t M, int64_t K) {
 
 // Launch over K range kr of rows a.K long: kr = a.K unsplit, a.K / S split
 // S ways (grid.y = S, each slice with its share of the resident workgroups).
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT = false>
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT = false,
+          bool ROWS = false>
 hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
+    const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / S : reg_grid(ntiles, W);
+    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / S : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
+    if (ROWS && (a.M <= 16 || a.M > 64 || ntiles <= grid)) return hipErrorInvalidValue;
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
     if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
     const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(a.M, kr);
@@ -795,12 +833,13 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT>),
+            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT>),
-                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(S)), dim3(64 * W), lds, a.stream,
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(S), static_cast<unsigned>(RB)),
+                       dim3(64 * W), lds, a.stream,
                        static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
                        static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
                        kr, a.K, a.part);
@@ -838,6 +877,14 @@ inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, i
 template <int DT, int BITS, int GS>
 hipError_t launch_reg_t(const MatmulArgs& a) {
     RegShape s;
+    if (a.M > 16) {
+        if (a.split > 1 || !reg_rows_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
+        if constexpr (BITS == 4) {
+            if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, false, true>(a, a.K);
+            if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, false, true>(a, a.K);
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.split > 1) {
         if (!reg_split_shape(BITS, GS, a.M, a.N, a.K, a.split, s)) return hipErrorInvalidValue;
         if constexpr (BITS == 4) {
@@ -869,9 +916,9 @@ hipError_t launch_reg_t(const MatmulArgs& a) {
 
 }  // namespace
 
-bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t K) {
-    if (M > 16) return false;
+bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t N, int64_t K) {
     RegShape s;
+    if (M > 16) return reg_rows_shape(bits, gs, M, N, K, s);
     return pick_shape(bits, gs, K, s);
 }
 

@@ -105,7 +105,13 @@ def test_kernel_supported():
     import torch
     f16 = torch.float16
     assert Q.kernel_supported(f16, 4, 64, 64, 4096, 4096, Q.KERNEL_VALU)
-    assert not Q.kernel_supported(f16, 4, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
+    # above 16 rows the register kernel needs 4-bit, K it covers and more tiles than row-block slots
+    assert Q.kernel_supported(f16, 4, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert Q.kernel_supported(f16, 4, 64, 64, 14336, 4096, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 4, 64, 17, 1024, 4096, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 8, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 4, 64, 17, 4096, 14336, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 4, 64, 65, 4096, 4096, Q.KERNEL_MFMA_REG)
     assert not Q.kernel_supported(f16, 4, 64, 4, 4096, 4096, 42)
     assert Q.qmm_kernel_supported(0, 5, 64, 4, 64, 256, 0) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_kernel_supported(0, 4, 64, -1, 64, 256, 0) == Q.QMM_ERR_INVALID_ARG
@@ -149,11 +155,12 @@ def test_probe_validation():
 
 def test_dispatch_follows_measured_crossovers():
     """qmm_select_kernel encodes the crossovers measured on MI355X
-    (affine_quantized_gemm_amd/sweep.py): M <= 16 -> the register-resident
-    MFMA kernel where it runs (K <= 4096), else the pass kernel; M > 16 -> the
-    64-column tile kernel for wide N, the 16-column tile kernel for M > 32
-    when N gives every CU a tile, the pass kernel otherwise (and wherever the
-    tile kernels cannot run)."""
+    (affine_quantized_gemm_amd/sweep.py): the register-resident MFMA kernel
+    wherever it runs (M <= 16 with K <= 4096; above 16 rows, 4-bit on row-block
+    grids when N has more tiles than their slots); otherwise M <= 16 -> the
+    pass kernel; M > 16 -> the 64-column tile kernel for wide N, the 16-column
+    tile kernel for M > 32 when N gives every CU a tile, the pass kernel
+    otherwise (and wherever the tile kernels cannot run)."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
     sel = lambda dt, b, gs, M, N, K: Q.kernel_name(Q.select_kernel(dt, b, gs, M, N, K))
@@ -163,10 +170,12 @@ def test_dispatch_follows_measured_crossovers():
         assert sel(bf16, 4, 64, M, 151936, 4096) == "mfma_splitfree_reg"
         assert sel(f16, 4, 64, M, 4096, 14336) == "mfma_splitfree_pass"
     for M in (17, 24, 32, 36, 48, 64):
-        assert sel(f16, 4, 64, M, 14336, 4096) == "mfma_splitfree_tile64"
+        assert sel(f16, 4, 64, M, 14336, 4096) == "mfma_splitfree_reg"
+        assert sel(f16, 4, 64, M, 4096, 4096) == "mfma_splitfree_reg"
+        assert sel(bf16, 4, 64, M, 151936, 4096) == "mfma_splitfree_reg"
         assert sel(bf16, 8, 64, M, 151936, 4096) == "mfma_splitfree_tile64"
-        for N, K in ((4096, 4096), (4096, 14336)):
-            assert sel(f16, 4, 64, M, N, K) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        assert sel(f16, 8, 64, M, 4096, 4096) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        assert sel(f16, 4, 64, M, 4096, 14336) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
         # fewer 16-column tiles than CUs: the pass kernel
         assert sel(f16, 4, 64, M, 1024, 4096) == "mfma_splitfree_pass"
         # K that is not a whole number of 4-bit k-blocks: the pass kernel
@@ -186,8 +195,8 @@ def test_split_plan_and_workspace_bytes():
     for M in (24, 32, 36, 48, 64):
         assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
         assert Q.workspace_bytes(f16, 4, 64, M, 4096, 14336) == 4 * M * 4096 * 4
-    # K = N = 4096: from M = 48
-    assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
+    # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace)
+    assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
     # N = 2048: 32 tiles -> 4 splits (capped)
     assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
     # M <= 16 on K the register kernel takes only split: 7 slices of 2048 (down), 2 of 4096 (K = 8192)

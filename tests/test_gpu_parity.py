@@ -300,6 +300,25 @@ def test_split_k(Q, kernel, dt, bits, gs):
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (M, split)
 
 
+@pytest.mark.parametrize("dt,gs,K", [("f16", 64, 4096), ("bf16", 32, 2048), ("bf16", 128, 4096)])
+def test_reg_row_blocks(Q, dt, gs, K):
+    """The register kernel above 16 rows: one 16-row block per workgroup
+    layer (the last one partial), every column tile of the slot, over a
+    ragged N (1027 tiles of 16); every output checked."""
+    N = 16 * 1027 + 5
+    w = synth.normal((N, K), 0.02, dt, 8500 + gs)
+    owq, osc, obi = oracle_quant(w, dt, 4, gs)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    for M in (17, 24, 32, 40, 48, 64):
+        print(f"reg rows {dt} gs{gs} M={M} N={N} K={K}", flush=True)
+        x = synth.normal((M, K), 1.0, dt, 8600 + M)
+        y = Q.small_m(x.cuda(), wq, sc, bi, 4, gs, kernel=Q.KERNEL_MFMA_REG)
+        torch.cuda.synchronize()
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, 4, gs)
+        ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+        assert ok, (M, worst)
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
