@@ -64,18 +64,19 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 // when N gives 32..64 tiles of 64 columns and M >= 24 (K >= 8192) or M >= 48,
 // into min(4, 256 / tiles) parts.
 //
-// M <= 16 with K the register kernel cannot take whole (the down
+// Before those: K the register kernel cannot take whole (the down
 // projection, K = 14336): that kernel on K / S slices, the fewest that work
-// (7 slices of 2048 at K = 14336): 13.7 / 15.0 / 16.1 us vs 16.1 / 18.3 /
-// 22.5 us for the split-free pass kernel at M = 1 / 8 / 16.
+// (7 slices of 2048 at K = 14336), on 16-row blocks above 16 rows: 13.7 /
+// 15.0 / 16.1 us vs 16.1 / 18.3 / 22.5 us for the split-free pass kernel at
+// M = 1 / 8 / 16, and 21.0 / 20.4 / 26.3 / 31.7 us vs 27.0 / 27.0 / 32.3 /
+// 36.6 us for the 64-column tile kernel split 4 ways at M = 24 / 32 / 48 /
+// 64.
 SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     SplitPlan p{select_kernel(dt, bits, gs, M, N, K), 1};
     if (p.kernel == QMM_KERNEL_MFMA_REG) return p;  // faster than any split measured
-    if (M <= 16) {
+    if (!mfma_reg_supports(bits, gs, 1, N, K))  // K deeper than the register kernel takes whole
         for (int s = 2; s <= 8; ++s)
             if (mfma_reg_split_supports(bits, gs, M, N, K, s)) return SplitPlan{QMM_KERNEL_MFMA_REG, s};
-        return p;
-    }
     if (!kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) return p;
     const int64_t ntiles = (N + 63) / 64;
     if (ntiles < 32 || ntiles > 64) return p;

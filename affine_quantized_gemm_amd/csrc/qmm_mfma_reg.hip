@@ -231,10 +231,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const int c = lane & 15;   // tile column of this lane's B operand / D output, row of its A operand
     const int jj = lane >> 4;  // k-slot quarter
     static_assert(!SPLIT || reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>(), "the K split runs the LDS-ring form");
-    static_assert(!ROWS || (reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() && !SPLIT && !MH),
-                  "row blocks run the LDS-ring form, unsplit, all 16 rows");
+    static_assert(!ROWS || (reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() && !MH),
+                  "row blocks run the LDS-ring form, all 16 rows");
+    const int m_all = M;  // rows of x and y (of each partial output when split)
+    int r0 = 0;           // first row of this workgroup's block
     if constexpr (ROWS) {
-        const int r0 = 16 * static_cast<int>(blockIdx.z);
+        r0 = 16 * static_cast<int>(blockIdx.z);
         x += static_cast<int64_t>(r0) * ldk;
         y += static_cast<int64_t>(r0) * N;
         M = M - r0 < 16 ? M - r0 : 16;
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 const int row = 4 * jj + q;
                 if (col < N && row < M) {
                     if constexpr (SPLIT)
-                        part[(static_cast<int64_t>(blockIdx.y) * M + row) * N + col] = v;
+                        part[(static_cast<int64_t>(blockIdx.y) * m_all + r0 + row) * N + col] = v;
                     else
                         y[static_cast<int64_t>(row) * N + col] = DtOps<DT>::rne(v);
                 }
@@ -824,7 +826,7 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / S : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
+    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / (S * RB) : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
     if (ROWS && (a.M <= 16 || a.M > 64 || ntiles <= grid)) return hipErrorInvalidValue;
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
     if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
@@ -864,21 +866,30 @@ hipError_t launch_shape(const MatmulArgs& a) {
 }
 
 // K split: the LDS-ring form (4-bit, vector form, 16 wavefronts) on slices
-// of K / split, each slice with 256 / split workgroups walking more column
-// tiles than that.
+// of K / split (and, above 16 rows, 16-row blocks), each (slice, row block)
+// with 256 / (split x blocks) workgroups walking more column tiles than that.
 inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, int split, RegShape& s) {
-    if (bits != 4 || M > 16 || split < 2 || K % split != 0) return false;
+    if (bits != 4 || M > 64 || split < 2 || K % split != 0) return false;
     if (!pick_shape(bits, gs, K / split, s) || !s.vec || s.W != 16) return false;
     const int64_t ntiles = (N + 15) / 16;
-    const int64_t per_slice = reg_grid(ntiles, 16) / split;
-    return per_slice >= 1 && ntiles > per_slice;
+    const int64_t per = reg_grid(ntiles, 16) / (split * ((M + 15) / 16));
+    return per >= 1 && ntiles > per;
 }
 
 template <int DT, int BITS, int GS>
 hipError_t launch_reg_t(const MatmulArgs& a) {
     RegShape s;
+    if (a.M > 16 && a.split > 1) {
+        if (!reg_split_shape(BITS, GS, a.M, a.N, a.K, a.split, s)) return hipErrorInvalidValue;
+        if constexpr (BITS == 4) {
+            const int64_t kr = a.K / a.split;
+            if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, true, true>(a, kr);
+            if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, true, true>(a, kr);
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.M > 16) {
-        if (a.split > 1 || !reg_rows_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
+        if (!reg_rows_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
         if constexpr (BITS == 4) {
             if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, false, true>(a, a.K);
             if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, false, true>(a, a.K);

@@ -185,20 +185,26 @@ def test_dispatch_follows_measured_crossovers():
 
 def test_split_plan_and_workspace_bytes():
     """The K-split plan of qmm_small_m_ws (crossovers measured with sweep.py
-    --splits): the 64-column tile kernel split min(4, 256 / tiles) ways when N
-    gives 32..64 such tiles and M >= 24 (K >= 8192) or M >= 48; at M <= 16 the
-    register kernel on the fewest K slices it covers, where it cannot take K
-    whole; otherwise no split and no workspace (exactly qmm_small_m)."""
+    --splits): the register kernel on the fewest K slices it covers where it
+    cannot take K whole (4-bit); else the 64-column tile kernel split
+    min(4, 256 / tiles) ways when N gives 32..64 such tiles and M >= 24
+    (K >= 8192) or M >= 48; otherwise no split and no workspace (exactly
+    qmm_small_m)."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
-    # down projection 4096 x 14336: 64 tiles -> 4 splits of 28 passes (7 each), from M = 24
+    # down projection 4096 x 14336, 4-bit: the register kernel on 7 K slices (row blocks above 16 rows)
     for M in (24, 32, 36, 48, 64):
-        assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
-        assert Q.workspace_bytes(f16, 4, 64, M, 4096, 14336) == 4 * M * 4096 * 4
+        assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_REG, 7)
+        assert Q.workspace_bytes(f16, 4, 64, M, 4096, 14336) == 7 * M * 4096 * 4
+    # 8-bit (no register split): 64 tiles of 64 columns -> 4 splits of 56 passes, from M = 24
+    for M in (24, 32, 36, 48, 64):
+        assert Q.split_plan(f16, 8, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+        assert Q.workspace_bytes(f16, 8, 64, M, 4096, 14336) == 4 * M * 4096 * 4
     # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace)
     assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
-    # N = 2048: 32 tiles -> 4 splits (capped)
-    assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+    # N = 2048: 32 tiles -> 4 splits (capped); 4-bit takes the register split
+    assert Q.split_plan(f16, 8, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
+    assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_REG, 7)
     # M <= 16 on K the register kernel takes only split: 7 slices of 2048 (down), 2 of 4096 (K = 8192)
     for M in (1, 8, 16):
         assert Q.split_plan(f16, 4, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_REG, 7)
@@ -219,7 +225,8 @@ def test_split_entry_validation():
     (fake addresses, no GPU)."""
     f16 = Q.QMM_F16
     base = (f16, 4, 64, 32, 4096, 14336, A, A, A, A, A)
-    need = 4 * 32 * 4096 * 4
+    need = 7 * 32 * 4096 * 4  # the plan: the register kernel on 7 K slices
+    assert Q.qmm_small_m_workspace_bytes(f16, 4, 64, 32, 4096, 14336) == need
     # workspace too small, missing, or misaligned
     assert Q.qmm_small_m_ws(*base, A, need - 4, None) == Q.QMM_ERR_INVALID_ARG
     assert Q.qmm_small_m_ws(*base, None, need, None) == Q.QMM_ERR_INVALID_ARG
@@ -233,7 +240,9 @@ def test_split_entry_validation():
     small = (f16, 4, 64, 8, 4096, 14336, A, A, A, A, A)
     assert Q.qmm_small_m_split_forced(*small, A, 7 * 8 * 4096 * 4, None, Q.KERNEL_MFMA_REG, 2) == \
         Q.QMM_ERR_UNSUPPORTED
-    assert Q.qmm_small_m_split_forced(*base, A, need, None, Q.KERNEL_MFMA_REG, 7) == Q.QMM_ERR_UNSUPPORTED
+    # (above 16 rows on row blocks too: 7 slices need 7 partial outputs, more than 4 hold)
+    assert Q.qmm_small_m_split_forced(*base, A, 4 * 32 * 4096 * 4, None, Q.KERNEL_MFMA_REG, 7) == \
+        Q.QMM_ERR_INVALID_ARG
     assert Q.qmm_small_m_split_forced(*small, A, 7 * 8 * 4096 * 4 - 4, None, Q.KERNEL_MFMA_REG, 7) == \
         Q.QMM_ERR_INVALID_ARG
     # the workspace a forced split needs is the reduced split's: 28 passes, split 5 -> 6 passes each -> 5 splits

@@ -323,13 +323,14 @@ def test_reg_row_blocks(Q, dt, gs, K):
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
     """The register kernel's K split (slices it covers, fp32 partials in the
-    workspace, fixed-order reduction) over a ragged N (258 tiles of 16), every
-    output checked; two runs bit-identical."""
+    workspace, fixed-order reduction; above 16 rows also on 16-row blocks)
+    over a ragged N (258 tiles of 16), every output checked; two runs
+    bit-identical."""
     N = 16 * 257 + 5
     w = synth.normal((N, K), 0.02, dt, 8000 + gs)
     owq, osc, obi = oracle_quant(w, dt, 4, gs)
     wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
-    for M in (1, 8, 16):
+    for M in (1, 8, 16, 24, 48, 64):
         x = synth.normal((M, K), 1.0, dt, 8100 + M)
         yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, 4, gs)
         for split in splits:
