@@ -56,13 +56,14 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 
 // K split (workspace entry point).  Measured on MI355X (sweep.py --splits,
 // graph-replayed): the 64-column tile kernel with K split 4 ways beats every
-// split-free variant on the 4096 x 14336 down projection from M = 24 (27.1
-// vs 37.9 us at M = 24, 37.0 vs 64.2 us at M = 64) and at K = N = 4096 from
-// M = 48 (16.8 vs 17.8, 18.6 vs 20.6 us); below that, with fewer than 32
-// such tiles (k/v, N = 1024: 14.5 vs 4.9 us at M = 8) or with 8 splits the
-// partial-sum pass costs more than the activation bytes it saves.  So: split
-// when N gives 32..64 tiles of 64 columns and M >= 24 (K >= 8192) or M >= 48,
-// into min(4, 256 / tiles) parts.
+// split-free variant from M = 24 when N gives 32..64 tiles of 64 columns
+// (down projection, 6/8-bit: it is the only split there; K = N = 4096,
+// 6/8-bit, M = 24 / 36: 15.9 / 17.3 us vs 18.5 / 20.0 us split-free); below
+// that, with fewer than 32 such tiles (k/v, N = 1024: 14.5 vs 4.9 us at
+// M = 8) or with 8 splits the partial-sum pass costs more than the
+// activation bytes it saves.  So: split when N gives 32..64 tiles of 64
+// columns and M >= 24, into min(4, 256 / tiles) parts.  (4-bit with K <=
+// 4096 takes the register kernel split-free, faster than any split.)
 //
 // Before those: K the register kernel cannot take whole (the down
 // projection, K = 14336): that kernel on K / S slices, the fewest that work
@@ -80,7 +81,7 @@ SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) 
     if (!kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) return p;
     const int64_t ntiles = (N + 63) / 64;
     if (ntiles < 32 || ntiles > 64) return p;
-    if (M < (K >= 8192 ? 24 : 48)) return p;
+    if (M < 24) return p;
     const int64_t want = 256 / ntiles < 4 ? 256 / ntiles : 4;
     const int split = tile_split(bits, K, TILE_CFG_64, static_cast<int>(want));
     if (split < 2) return p;

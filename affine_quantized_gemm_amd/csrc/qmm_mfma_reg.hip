@@ -248,6 +248,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         scales += sk / GS;
         biases += sk / GS;
     }
+    if constexpr (!SPLIT) ldk = K;  // (unsplit: the same value, known to the compiler as K)
     const int64_t row_words = ldk * BITS / 32;
     const int64_t G = K / GS;     // groups of a row within the K range (the LDS block layout)
     const int64_t Gf = ldk / GS;  // scale/bias row stride

@@ -187,9 +187,8 @@ def test_split_plan_and_workspace_bytes():
     """The K-split plan of qmm_small_m_ws (crossovers measured with sweep.py
     --splits): the register kernel on the fewest K slices it covers where it
     cannot take K whole (4-bit); else the 64-column tile kernel split
-    min(4, 256 / tiles) ways when N gives 32..64 such tiles and M >= 24
-    (K >= 8192) or M >= 48; otherwise no split and no workspace (exactly
-    qmm_small_m)."""
+    min(4, 256 / tiles) ways when N gives 32..64 such tiles and M >= 24;
+    otherwise no split and no workspace (exactly qmm_small_m)."""
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
     # down projection 4096 x 14336, 4-bit: the register kernel on 7 K slices (row blocks above 16 rows)
@@ -200,8 +199,12 @@ def test_split_plan_and_workspace_bytes():
     for M in (24, 32, 36, 48, 64):
         assert Q.split_plan(f16, 8, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
         assert Q.workspace_bytes(f16, 8, 64, M, 4096, 14336) == 4 * M * 4096 * 4
-    # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace)
+    # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace);
+    # 6/8-bit there: the 64-column tile kernel split 4 ways from M = 24
     assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
+    for M in (24, 36, 64):
+        assert Q.split_plan(f16, 8, 64, M, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
+        assert Q.split_plan(bf16, 6, 128, M, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
     # N = 2048: 32 tiles -> 4 splits (capped); 4-bit takes the register split
     assert Q.split_plan(f16, 8, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
     assert Q.split_plan(f16, 4, 64, 64, 2048, 14336) == (Q.KERNEL_MFMA_REG, 7)
