@@ -827,7 +827,7 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = SPLIT ? reg_grid(ntiles, W) / (S * RB) : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
+    const int64_t grid = SPLIT ? 256 * (16 / W) / (S * RB) : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
     if (ROWS && (a.M <= 16 || a.M > 64 || ntiles <= grid)) return hipErrorInvalidValue;
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
     if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
@@ -873,7 +873,7 @@ inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, i
     if (bits != 4 || M > 64 || split < 2 || K % split != 0) return false;
     if (!pick_shape(bits, gs, K / split, s) || !s.vec || s.W != 16) return false;
     const int64_t ntiles = (N + 15) / 16;
-    const int64_t per = reg_grid(ntiles, 16) / (split * ((M + 15) / 16));
+    const int64_t per = 256 * (16 / s.W) / (split * ((M + 15) / 16));  // resident workgroups per (slice, block)
     return per >= 1 && ntiles > per;
 }
 
