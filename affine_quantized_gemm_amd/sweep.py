@@ -8,7 +8,14 @@ events on the replay stream.  The fastest
 variant per (shape, M) is what ``qmm_select_kernel`` should return; the
 measured table is the source of the crossovers compiled into the dispatch.
 
-    python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...] [--splits]
+    python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...] [--splits] [--layer]
+
+``--layer`` adds a synthetic decoder layer at the page's projection shapes
+(hidden 4096, intermediate 14336: q and o 4096 -> 4096, k and v 4096 -> 1024,
+gate and up 4096 -> 14336, down 14336 -> 4096; random weights, so only the
+shape of the step-time curve over M is reproduced, not a model's numbers):
+per M, the sum of the seven calls with the variant qmm_small_m selects, and
+with qmm_small_m_ws's plan where it takes a split.
 
 The pages' own dispatch story is a crossover curve in M, measured per shape
 (MLX issue #4720, "Root cause" and the M-sweep table under "Measurements").
@@ -139,21 +146,54 @@ def sweep_shape(name, ms, stack_mib, splits=False):
     return rows
 
 
+# (shape, calls per layer): q, o -> verify; k, v -> kv; gate, up -> gateup; down
+LAYER = (("verify", 2), ("kv", 2), ("gateup", 2), ("down", 1))
+
+
+def layer_table(rows):
+    """Per-M sums of one decoder layer's seven projection calls, from the
+    measured rows (split-free selection, and with the workspace plan)."""
+    by = {(r["shape"], r["M"]): r for r in rows}
+    out = []
+    for M in sorted({r["M"] for r in rows}):
+        if not all((name, M) in by for name, _ in LAYER):
+            continue
+        sel = ws = 0.0
+        for name, n in LAYER:
+            r = by[(name, M)]
+            t = r["us"][r["selected"]]
+            sel += n * t
+            ws += n * r.get("split_us", {}).get("planned_ws", t)
+        out.append({"M": M, "layer_us": round(sel, 2), "layer_ws_us": round(ws, 2)})
+    return out
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--shapes", default=",".join(SHAPES))
     p.add_argument("--ms", default=",".join(map(str, MS)))
     p.add_argument("--stack-mib", type=int, default=576)
     p.add_argument("--json", default=None)
-    p.add_argument("--splits", action="store_true", help="also time K splits of the tile kernels (workspace path)")
+    p.add_argument("--splits", action="store_true", help="also time K splits (workspace path)")
+    p.add_argument("--layer", action="store_true", help="also sum one decoder layer's projections per M")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
+    shapes = a.shapes.split(",")
+    if a.layer:
+        shapes += [name for name, _ in LAYER if name not in shapes]
     rows = []
-    for name in a.shapes.split(","):
+    for name in shapes:
         rows += sweep_shape(name, ms, a.stack_mib, a.splits)
+    out = rows
+    if a.layer:
+        table = layer_table(rows)
+        for t in table:
+            print(f"layer  M={t['M']:3d}  {t['layer_us']:8.2f} us  (with the workspace plan {t['layer_ws_us']:8.2f} us)",
+                  flush=True)
+        out = {"rows": rows, "layer": table}
     if a.json:
         with open(a.json, "w") as f:
-            json.dump(rows, f, indent=1)
+            json.dump(out, f, indent=1)
 
 
 if __name__ == "__main__":
