@@ -29,14 +29,21 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
 //     M = 24 / 32 / 64 on the 14336 x 4096 gate/up projection, 9.5 / 11.3 /
 //     11.9 us vs 12.9 (pass) / 16.0 / 20.6 (16-column tiles) at M = 24 / 36 /
 //     64, K = N = 4096, 99 / 188 us vs 190 / 287 us on the LM head;
-//   * otherwise, M > 16, wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
+//   * M 17..64 where 16 rows take one tile per workgroup (N up to 4096 at
+//     K <= 4096, any width): the register kernel on a grid of tiles x 16-row
+//     blocks: 5.6 / 6.0 us vs 7.9 / 8.1 us (pass) at M = 24 / 64 on the
+//     1024 x 4096 k/v projection; 8-bit K = N = 4096: 12.0 / 16.5 / 21.6 us
+//     vs 17.3 / 19.9 / 27.9 us (16-column tiles) at M = 24 / 36 / 64, 6-bit
+//     gs128 11.8 / 16.6 / 22.5 us vs 17.2 (pass) / 20.0 / 29.0 us;
+//   * otherwise (6/8-bit with more tiles than resident workgroups), M > 16,
+//     wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
 //     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
 //     projection, 186 / 278 us vs 368 / 669 us on the 151936-column LM head;
 //   * M > 32, N from 4096 (at least one 16-column tile per CU): the
 //     16-column tile kernel: 46.0 / 64.7 us vs 56.1 / 65.5 us (pass) at
-//     M = 36 / 64 on the down projection, 16.1 / 20.3 us vs 21.6 / 21.9 us at
-//     K = N = 4096; with fewer tiles than CUs it idles most of the chip
-//     (15.7 us vs 7.8 us for the pass kernel at M = 36, N = 1024);
+//     M = 36 / 64 on the down projection; with fewer tiles than CUs it idles
+//     most of the chip (15.7 us vs 7.8 us for the pass kernel at M = 36,
+//     N = 1024);
 //   * everything else (M = 17..32 with N < 8192, or K the tile kernels do not
 //     take): the pass kernel (37.3 us vs 47.7 us for the 16-column tiles at
 //     M = 32 on the down projection);
@@ -55,15 +62,20 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 }
 
 // K split (workspace entry point).  Measured on MI355X (sweep.py --splits,
-// graph-replayed): the 64-column tile kernel with K split 4 ways beats every
-// split-free variant from M = 24 when N gives 32..64 tiles of 64 columns
-// (down projection, 6/8-bit: it is the only split there; K = N = 4096,
-// 6/8-bit, M = 24 / 36: 15.9 / 17.3 us vs 18.5 / 20.0 us split-free); below
+// graph-replayed): the 64-column tile kernel with K split 4 ways beats the
+// other split-free variants from M = 24 when N gives 32..64 tiles of 64
+// columns (down projection, 6/8-bit: it is the only split there); below
 // that, with fewer than 32 such tiles (k/v, N = 1024: 14.5 vs 4.9 us at
 // M = 8) or with 8 splits the partial-sum pass costs more than the
 // activation bytes it saves.  So: split when N gives 32..64 tiles of 64
-// columns and M >= 24, into min(4, 256 / tiles) parts.  (4-bit with K <=
-// 4096 takes the register kernel split-free, faster than any split.)
+// columns and M >= 24, into min(4, 256 / tiles) parts.
+//
+// Where the register kernel runs split-free it is faster than any split
+// (4-bit with K <= 4096; 6/8-bit K = N = 4096 at M = 24 / 36: 12.0 / 16.5 us
+// vs 15.9 / 17.7 us split, 8-bit), except its single-tile row blocks above
+// 48 rows (4 blocks, 4 workgroups per tile): there the split wins where it
+// applies (6/8-bit K = N = 4096 at M = 64: 21.1 / 19.5 us vs 22.5 / 21.6 us;
+// at M = 48 the row blocks still win, 17.2 vs 18.1 us at 8-bit).
 //
 // Before those: K the register kernel cannot take whole (the down
 // projection, K = 14336): that kernel on K / S slices, the fewest that work
@@ -74,7 +86,8 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 // 64.
 SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     SplitPlan p{select_kernel(dt, bits, gs, M, N, K), 1};
-    if (p.kernel == QMM_KERNEL_MFMA_REG) return p;  // faster than any split measured
+    if (p.kernel == QMM_KERNEL_MFMA_REG && !(M > 48 && mfma_reg_single_tile_rows(bits, gs, M, N, K)))
+        return p;  // faster than any split measured
     if (!mfma_reg_supports(bits, gs, 1, N, K))  // K deeper than the register kernel takes whole
         for (int s = 2; s <= 8; ++s)
             if (mfma_reg_split_supports(bits, gs, M, N, K, s)) return SplitPlan{QMM_KERNEL_MFMA_REG, s};

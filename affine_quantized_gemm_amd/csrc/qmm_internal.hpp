@@ -34,9 +34,13 @@ hipError_t launch_mfma_pass(const MatmulArgs& a);
 // tile kernel shapes (columns per workgroup tile)
 enum { TILE_CFG_16 = 0, TILE_CFG_64 = 1 };
 hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg);
-// M <= 16: every format where the k-blocks fit; M 17..64: 4-bit row-block
-// grids on shapes with more 16-column tiles than column slots.
+// M <= 16: every format where the k-blocks fit; M 17..64, on 16-row blocks
+// (vector form, 16 wavefronts): 4-bit LDS-ring grids on shapes with more
+// 16-column tiles than column slots, else any width where 16 rows take one
+// tile per workgroup.
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t N, int64_t K);
+// the second of those (one tile per workgroup, 16-row blocks)
+bool mfma_reg_single_tile_rows(int bits, int gs, int64_t M, int64_t N, int64_t K);
 // The register kernel's K split (4-bit LDS-ring form): K a whole number
 // `split` of slices that form covers, with more column tiles than
 // workgroups per slice.

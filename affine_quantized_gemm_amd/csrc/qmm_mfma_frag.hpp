@@ -233,12 +233,17 @@ __device__ __forceinline__ void segment_frags(uint32_t (&w)[NW], Frag (&b)[NS], 
     }
 }
 
-template <int BITS, int NW>
+template <int BITS, int NW, bool NT = true>
 __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ p, uint32_t (&w)[NW]) {
     if constexpr (NW == 4) {
         // streamed once: the non-temporal hint keeps the weights from
-        // displacing reused data in the caches
-        const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        // displacing reused data in the caches (NT = false: read again by
+        // other workgroups, so kept in L2)
+        u32x4_t a;
+        if constexpr (NT)
+            a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        else
+            a = *reinterpret_cast<const u32x4_t*>(p);
         w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
     } else {
         const uint3 a = *reinterpret_cast<const uint3*>(p);

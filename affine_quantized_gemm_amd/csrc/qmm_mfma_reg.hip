@@ -199,11 +199,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // fp32 partial output in part[s][M][N] instead of y; a second kernel adds
 // the slices in order.  Unsplit: ldk = K, part unused.
 //
-// Row blocks (ROWS, LDS-ring form, not with SPLIT): M up to 64, workgroup
-// (., ., z) computes rows [16 z, 16 z + 16) -- its own activation rows,
-// every column tile of its slot.  The row blocks of a column slot are
-// resident together on one XCD (linear workgroup ids congruent mod 8), so a
-// tile's weights come from HBM once and from that XCD's L2 for the others.
+// Row blocks (ROWS, not with SPLIT): M up to 64, workgroup (., ., z)
+// computes rows [16 z, 16 z + 16) -- its own activation rows -- of every
+// column tile of its slot (LDS-ring form) or of its one tile (single-tile
+// form).  The row blocks of a column slot or tile have linear workgroup ids
+// congruent mod 8, so they run on one XCD: a tile's weights come from HBM
+// once and from that XCD's L2 for the others (cached loads, not streamed).
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
@@ -224,15 +225,16 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     // partial-tile buffers: lanes stored per row quarter (rows 0..7 only: 32)
     constexpr int PL = DMA && MH ? 32 : 64;
     static_assert(!DMA || COOP, "the weight ring carries the cooperative scale/bias blocks");
-    const int wave_lds = DMA ? dma_wave_lds(MH) : wave_lds_bytes(M, KPW, F::KBLK);
+    // (row blocks: sized for a whole block, the same in every workgroup)
+    const int wave_lds = DMA ? dma_wave_lds(MH) : wave_lds_bytes(ROWS ? 16 : M, KPW, F::KBLK);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15;   // tile column of this lane's B operand / D output, row of its A operand
     const int jj = lane >> 4;  // k-slot quarter
     static_assert(!SPLIT || reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>(), "the K split runs the LDS-ring form");
-    static_assert(!ROWS || (reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() && !MH),
-                  "row blocks run the LDS-ring form, all 16 rows");
+    static_assert(!ROWS || ((reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() || !MULTI) && !MH),
+                  "row blocks run the LDS-ring form or one tile per workgroup, all 16 rows");
     const int m_all = M;  // rows of x and y (of each partial output when split)
     int r0 = 0;           // first row of this workgroup's block
     if constexpr (ROWS) {
@@ -374,12 +376,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         for (int i = 0; i < KPW; ++i) {
             if constexpr (VEC) {
                 // VEC: the k-blocks cover K exactly
-                load_segment<BITS, F::SEG_WORDS>(
+                load_segment<BITS, F::SEG_WORDS, !ROWS>(
                     reinterpret_cast<const uint32_t*>(wbase + w_off + i * (F::KBLK * BITS / 8)), r.w[i]);
             } else {
                 int64_t code0 = (kb0 + i) * F::KBLK + jj * F::SEG;
                 code0 = code0 < K ? code0 : K - F::SEG;
-                load_segment<BITS, F::SEG_WORDS>(
+                load_segment<BITS, F::SEG_WORDS, !ROWS>(
                     reinterpret_cast<const uint32_t*>(wbase + lane_row * row_bytes + code0 * BITS / 8), r.w[i]);
             }
         }
@@ -806,6 +808,17 @@ inline bool reg_rows_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, Re
     return (N + 15) / 16 > reg_rows_grid(static_cast<int>((M + 15) / 16));
 }
 
+// Row blocks, one tile per workgroup (M 17..64, any width, vector form, 16
+// wavefronts): where the shape at 16 rows is single-tile (no more column
+// tiles than resident workgroups) and the LDS-ring row blocks do not apply;
+// the grid is tiles x blocks.
+inline bool reg_rows1_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, RegShape& s) {
+    if (M <= 16 || M > 64 || reg_rows_shape(bits, gs, M, N, K, s)) return false;
+    if (!pick_shape(bits, gs, K, s) || !s.vec || s.W != 16) return false;
+    const int64_t ntiles = (N + 15) / 16;
+    return ntiles <= reg_grid(ntiles, s.W);
+}
+
 // dynamic LDS bytes of one workgroup
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH>
 size_t reg_lds_bytes(int64_t M, int64_t K) {
@@ -827,11 +840,14 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = SPLIT ? 256 * (16 / W) / (S * RB) : ROWS ? reg_rows_grid(RB) : reg_grid(ntiles, W);
-    if (ROWS && (a.M <= 16 || a.M > 64 || ntiles <= grid)) return hipErrorInvalidValue;
+    const int64_t grid = SPLIT  ? 256 * (16 / W) / (S * RB)
+                         : ROWS ? (MULTI ? reg_rows_grid(RB) : ntiles)
+                                : reg_grid(ntiles, W);
+    if (ROWS && (a.M <= 16 || a.M > 64 || (MULTI ? ntiles <= grid : ntiles > reg_grid(ntiles, W))))
+        return hipErrorInvalidValue;
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
     if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
-    const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(a.M, kr);
+    const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(ROWS ? 16 : a.M, kr);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     if (lds > 65536) {
         // above the default dynamic-LDS limit: raise it once per kernel
@@ -890,11 +906,18 @@ hipError_t launch_reg_t(const MatmulArgs& a) {
         return hipErrorInvalidValue;
     }
     if (a.M > 16) {
-        if (!reg_rows_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
-        if constexpr (BITS == 4) {
-            if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, false, true>(a, a.K);
-            if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, false, true>(a, a.K);
+        if (reg_rows_shape(BITS, GS, a.M, a.N, a.K, s)) {
+            if constexpr (BITS == 4) {
+                if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, true, false, false, true>(a, a.K);
+                if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, true, false, false, true>(a, a.K);
+            }
+            return hipErrorInvalidValue;
         }
+        if (!reg_rows1_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
+        if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, false, false, false, true>(a, a.K);
+        if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, false, false, false, true>(a, a.K);
+        if constexpr (BITS != 4)
+            if (s.KPW == 4) return launch_shape_m<DT, BITS, GS, 16, 4, true, false, false, false, true>(a, a.K);
         return hipErrorInvalidValue;
     }
     if (a.split > 1) {
@@ -930,8 +953,13 @@ hipError_t launch_reg_t(const MatmulArgs& a) {
 
 bool mfma_reg_supports(int bits, int gs, int64_t M, int64_t N, int64_t K) {
     RegShape s;
-    if (M > 16) return reg_rows_shape(bits, gs, M, N, K, s);
+    if (M > 16) return reg_rows_shape(bits, gs, M, N, K, s) || reg_rows1_shape(bits, gs, M, N, K, s);
     return pick_shape(bits, gs, K, s);
+}
+
+bool mfma_reg_single_tile_rows(int bits, int gs, int64_t M, int64_t N, int64_t K) {
+    RegShape s;
+    return reg_rows1_shape(bits, gs, M, N, K, s);
 }
 
 bool mfma_reg_split_supports(int bits, int gs, int64_t M, int64_t N, int64_t K, int split) {

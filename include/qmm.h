@@ -79,7 +79,7 @@ enum qmm_status {
 /* Kernel variants for qmm_small_m_forced / qmm_select_kernel. */
 enum qmm_kernel {
     QMM_KERNEL_VALU = 0,      /* split-free, VALU dot products, cross-lane K reduction */
-    QMM_KERNEL_MFMA_REG = 1,  /* split-free, MFMA with in-register weight fragments, M <= 16 */
+    QMM_KERNEL_MFMA_REG = 1,  /* split-free, MFMA with in-register weight fragments (16-row blocks above 16 rows) */
     QMM_KERNEL_MFMA_PASS = 2, /* split-free, MFMA, K walked in passes of 16 k-blocks, any K, M <= 64 */
     QMM_KERNEL_MFMA_TILE16 = 3, /* split-free, MFMA, 16-column tiles, activations shared through LDS, M <= 64 */
     QMM_KERNEL_MFMA_TILE64 = 4, /* as TILE16 with 64-column tiles (wide N) */
@@ -116,8 +116,12 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
 
 /* As qmm_small_m with the variant forced (measurement and tests).
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
- * (QMM_KERNEL_MFMA_REG needs M <= 16 and K <= 4096; the TILE variants need
- * K to be a multiple of 128 for 4-bit codes, of 64 for 6- and 8-bit). */
+ * (QMM_KERNEL_MFMA_REG needs K <= 4096; for M = 17..64 it runs on 16-row
+ * blocks and needs K to fill 16 wavefronts with whole k-blocks (above 1024
+ * for 4-bit codes, above 512 for 6/8-bit) and N either to give more 4-bit
+ * 16-column tiles than its row-block slots or at most one tile per resident
+ * workgroup -- qmm_kernel_supported says which shapes; the TILE variants
+ * need K to be a multiple of 128 for 4-bit codes, of 64 for 6- and 8-bit). */
 int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
                        const void* x, const uint32_t* wq, const void* scales,
                        const void* biases, void* y, void* stream, int kernel_id);

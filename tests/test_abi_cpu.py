@@ -105,11 +105,17 @@ def test_kernel_supported():
     import torch
     f16 = torch.float16
     assert Q.kernel_supported(f16, 4, 64, 64, 4096, 4096, Q.KERNEL_VALU)
-    # above 16 rows the register kernel needs 4-bit, K it covers and more tiles than row-block slots
+    # above 16 rows the register kernel runs on 16-row blocks: 4-bit with more tiles than
+    # row-block slots, or any width with at most one tile per resident workgroup; K it covers
+    # with 16 wavefronts
     assert Q.kernel_supported(f16, 4, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
     assert Q.kernel_supported(f16, 4, 64, 64, 14336, 4096, Q.KERNEL_MFMA_REG)
-    assert not Q.kernel_supported(f16, 4, 64, 17, 1024, 4096, Q.KERNEL_MFMA_REG)
-    assert not Q.kernel_supported(f16, 8, 64, 17, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert Q.kernel_supported(f16, 4, 64, 17, 1024, 4096, Q.KERNEL_MFMA_REG)
+    assert Q.kernel_supported(f16, 8, 64, 64, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert Q.kernel_supported(f16, 6, 128, 40, 4096, 4096, Q.KERNEL_MFMA_REG)
+    assert not Q.kernel_supported(f16, 8, 64, 17, 14336, 4096, Q.KERNEL_MFMA_REG)  # 8-bit, 896 tiles
+    assert not Q.kernel_supported(f16, 4, 64, 17, 4096, 1024, Q.KERNEL_MFMA_REG)  # 8 wavefronts
+    assert Q.kernel_supported(f16, 4, 64, 16, 4096, 1024, Q.KERNEL_MFMA_REG)
     assert not Q.kernel_supported(f16, 4, 64, 17, 4096, 14336, Q.KERNEL_MFMA_REG)
     assert not Q.kernel_supported(f16, 4, 64, 65, 4096, 4096, Q.KERNEL_MFMA_REG)
     assert not Q.kernel_supported(f16, 4, 64, 4, 4096, 4096, 42)
@@ -156,8 +162,9 @@ def test_probe_validation():
 def test_dispatch_follows_measured_crossovers():
     """qmm_select_kernel encodes the crossovers measured on MI355X
     (affine_quantized_gemm_amd/sweep.py): the register-resident MFMA kernel
-    wherever it runs (M <= 16 with K <= 4096; above 16 rows, 4-bit on row-block
-    grids when N has more tiles than their slots); otherwise M <= 16 -> the
+    wherever it runs (M <= 16 with K <= 4096; above 16 rows on 16-row blocks:
+    4-bit when N has more tiles than their slots, any width when 16 rows take
+    one tile per workgroup); otherwise M <= 16 -> the
     pass kernel; M > 16 -> the 64-column tile kernel for wide N, the 16-column
     tile kernel for M > 32 when N gives every CU a tile, the pass kernel
     otherwise (and wherever the tile kernels cannot run)."""
@@ -174,10 +181,15 @@ def test_dispatch_follows_measured_crossovers():
         assert sel(f16, 4, 64, M, 4096, 4096) == "mfma_splitfree_reg"
         assert sel(bf16, 4, 64, M, 151936, 4096) == "mfma_splitfree_reg"
         assert sel(bf16, 8, 64, M, 151936, 4096) == "mfma_splitfree_tile64"
-        assert sel(f16, 8, 64, M, 4096, 4096) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        # 16 rows take one tile per workgroup: the register kernel on tiles x row blocks
+        assert sel(f16, 8, 64, M, 4096, 4096) == "mfma_splitfree_reg"
+        assert sel(bf16, 6, 128, M, 4096, 4096) == "mfma_splitfree_reg"
+        assert sel(f16, 4, 64, M, 1024, 4096) == "mfma_splitfree_reg"
         assert sel(f16, 4, 64, M, 4096, 14336) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
-        # fewer 16-column tiles than CUs: the pass kernel
-        assert sel(f16, 4, 64, M, 1024, 4096) == "mfma_splitfree_pass"
+        # 6/8-bit with more tiles than resident workgroups, N >= 4096 but < 8192
+        assert sel(f16, 8, 64, M, 6144, 4096) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        # fewer 16-column tiles than CUs, K the register kernel does not take: the pass kernel
+        assert sel(f16, 4, 64, M, 1024, 4160) == "mfma_splitfree_pass"
         # K that is not a whole number of 4-bit k-blocks: the pass kernel
         assert sel(f16, 4, 64, M, 14336, 4160) == "mfma_splitfree_pass"
     assert sel(f16, 6, 64, 40, 4096, 4160) == "mfma_splitfree_tile16"   # 6-bit k-blocks are 64 codes
@@ -199,10 +211,15 @@ def test_split_plan_and_workspace_bytes():
     for M in (24, 32, 36, 48, 64):
         assert Q.split_plan(f16, 8, 64, M, 4096, 14336) == (Q.KERNEL_MFMA_TILE64, 4)
         assert Q.workspace_bytes(f16, 8, 64, M, 4096, 14336) == 4 * M * 4096 * 4
-    # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace);
-    # 6/8-bit there: the 64-column tile kernel split 4 ways from M = 24
+    # K = N = 4096: the register kernel on row blocks is faster than any split (no workspace),
+    # except its single-tile row blocks above 48 rows (6/8-bit): the 64-column tile kernel
+    # split 4 ways
     assert Q.split_plan(f16, 4, 64, 48, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
-    for M in (24, 36, 64):
+    assert Q.split_plan(f16, 4, 64, 64, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
+    for M in (24, 36, 48):
+        assert Q.split_plan(f16, 8, 64, M, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
+        assert Q.split_plan(bf16, 6, 128, M, 4096, 4096) == (Q.KERNEL_MFMA_REG, 1)
+    for M in (49, 64):
         assert Q.split_plan(f16, 8, 64, M, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
         assert Q.split_plan(bf16, 6, 128, M, 4096, 4096) == (Q.KERNEL_MFMA_TILE64, 4)
     # N = 2048: 32 tiles -> 4 splits (capped); 4-bit takes the register split

@@ -319,6 +319,31 @@ def test_reg_row_blocks(Q, dt, gs, K):
         assert ok, (M, worst)
 
 
+@pytest.mark.parametrize("dt,bits,gs,K,N", [("f16", 4, 64, 4096, 1024), ("bf16", 8, 64, 4096, 16 * 255 + 7),
+                                            ("f16", 6, 128, 4096, 4096), ("bf16", 6, 32, 2048, 1000),
+                                            ("f16", 8, 32, 4096, 515), ("bf16", 4, 64, 2048, 9)])
+def test_reg_row_blocks_single_tile(Q, dt, bits, gs, K, N):
+    """The register kernel above 16 rows where 16 rows take one tile per
+    workgroup: a grid of tiles x 16-row blocks (the last block partial),
+    ragged and narrow N; every output checked, and each row block
+    bit-identical to the same rows computed alone."""
+    w = synth.normal((N, K), 0.02, dt, 8700 + bits * 10 + gs)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    for M in (17, 24, 33, 48, 64):
+        print(f"reg rows single-tile {dt} {bits}-bit gs{gs} M={M} N={N} K={K}", flush=True)
+        x = synth.normal((M, K), 1.0, dt, 8800 + M)
+        xc = x.cuda()
+        y = Q.small_m(xc, wq, sc, bi, bits, gs, kernel=Q.KERNEL_MFMA_REG)
+        torch.cuda.synchronize()
+        yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+        ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+        assert ok, (M, worst)
+        for r0 in range(0, M, 16):
+            yb = Q.small_m(xc[r0:r0 + 16].contiguous(), wq, sc, bi, bits, gs, kernel=Q.KERNEL_MFMA_REG)
+            assert torch.equal(y[r0:r0 + 16].view(torch.int16), yb.view(torch.int16)), (M, r0)
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
