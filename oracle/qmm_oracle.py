@@ -17,6 +17,9 @@ What it computes (sources are the web pages this project is built from):
   MTPLX", section "Implementation and Configuration" (the usage example).
 * The transposed product y = x . dequant(W)^T with W stored [N, K] -- MLX
   issue #4720, "To Reproduce" (``quantized_matmul(..., transpose=True)``).
+* The batched form, one weight matrix per batch entry (the adjacent API
+  case to the transposed, non-batched call of MLX issue #4720, "Describe the
+  bug").
 * Weight bytes per call = packed words + 4 bytes of scale/bias per group --
   MLX issue #4720, "To Reproduce" (the ``wbytes`` expression).
 
@@ -251,6 +254,24 @@ def qmm(x, wq, scales, biases, dt: str, bits: int, group_size: int, row_chunk: i
         w64 = dequantize_exact(wq[r0:r1], scales[r0:r1], biases[r0:r1], dt, bits, group_size, K)
         y[:, r0:r1] = x64 @ w64.T
         T[:, r0:r1] = ax @ np.abs(w64).T
+    return y, T
+
+
+def qmm_batched(x, wq, scales, biases, dt: str, bits: int, group_size: int):
+    """Batched product with weights per batch entry: y[b] = x[b] . dequant(W[b])^T.
+
+    MLX issue #4720, "Describe the bug", singles out transposed, non-batched
+    calls; this is the batched form of the same product.  x is [B, M, K],
+    wq [B, N, words], scales and biases [B, N, K/gs]; entry b uses only the
+    b-th slice of each.  Returns (y [B, M, N], T [B, M, N]) as :func:`qmm`
+    does for each entry.
+    """
+    B = x.shape[0]
+    M, N = x.shape[1], wq.shape[1]
+    y = np.empty((B, M, N), dtype=np.float64)
+    T = np.empty((B, M, N), dtype=np.float64)
+    for b in range(B):
+        y[b], T[b] = qmm(x[b], wq[b], scales[b], biases[b], dt, bits, group_size)
     return y, T
 
 

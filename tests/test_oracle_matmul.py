@@ -109,3 +109,59 @@ def test_tolerance_rule():
     assert not ok
     ok, _ = O.within_tolerance(np.array([[np.nan, -2.0]]), y_o, T)
     assert not ok
+
+
+# ---------------------------------------------------------------------------
+# batched form: one weight matrix per batch entry
+# ---------------------------------------------------------------------------
+
+def _scaled(a, dt, factor):
+    """a * factor in the dtype (a power of two: exact for these magnitudes)."""
+    return O.f32_to_dt_rne((O.to_f32(a, dt) * np.float32(factor)).astype(np.float32), dt)
+
+
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 4, 64), ("bf16", 8, 32), ("bf16", 6, 128)])
+def test_batched_entries_use_their_own_weights_and_rows(dt, bits, gs):
+    """Entry b with weights 2^b W quantizes to the same codes with 2^b the
+    scales and biases, so its output is exactly 2^b times entry 0's; with
+    activations 2^b x likewise.  A batched product that reads another
+    entry's weights or rows breaks one of the two."""
+    B, M, N, K = 4, 3, 5, 2 * gs
+    w = synth.to_oracle(synth.normal((N, K), 0.02, dt, 81))
+    x = synth.to_oracle(synth.normal((M, K), 1.0, dt, 82))
+    ws = [_scaled(w, dt, 2.0 ** b) for b in range(B)]
+    qs = [O.quantize(wb, dt, bits, gs) for wb in ws]
+    for b in range(1, B):
+        assert np.array_equal(qs[b][0], qs[0][0])
+        assert np.array_equal(O.to_f64(qs[b][1], dt), 2.0 ** b * O.to_f64(qs[0][1], dt))
+    wq, sc, bi = (np.stack([q[i] for q in qs]) for i in range(3))
+    y, T = O.qmm_batched(np.stack([x] * B), wq, sc, bi, dt, bits, gs)
+    assert y.shape == (B, M, N) and T.shape == (B, M, N)
+    for b in range(B):
+        assert np.array_equal(y[b], 2.0 ** b * y[0]) and np.array_equal(T[b], 2.0 ** b * T[0])
+    xs = np.stack([_scaled(x, dt, 2.0 ** b) for b in range(B)])
+    y2, _ = O.qmm_batched(xs, np.stack([qs[0][0]] * B), np.stack([qs[0][1]] * B), np.stack([qs[0][2]] * B),
+                          dt, bits, gs)
+    for b in range(B):
+        assert np.array_equal(y2[b], 2.0 ** b * y2[0])
+    assert np.array_equal(y2[0], y[0])
+
+
+def test_batched_exact_rationals():
+    """Independent entries against exact rational sums (big-integer unpack)."""
+    dt, bits, gs = "f16", 4, 32
+    B, M, N, K = 3, 2, 3, 64
+    xs, wqs, scs, bis = [], [], [], []
+    for b in range(B):
+        x, wq, sc, bi = make(dt, bits, gs, M, N, K, 90 + 2 * b)
+        xs.append(x); wqs.append(wq); scs.append(sc); bis.append(bi)
+    y, _ = O.qmm_batched(np.stack(xs), np.stack(wqs), np.stack(scs), np.stack(bis), dt, bits, gs)
+    for b in range(B):
+        xf, s, bb = O.to_f64(xs[b], dt), O.to_f64(scs[b], dt), O.to_f64(bis[b], dt)
+        for n in range(N):
+            q = bigint_unpack_row(wqs[b][n], bits, K)
+            wh = [Fraction(float(s[n, k // gs])) * q[k] + Fraction(float(bb[n, k // gs])) for k in range(K)]
+            for m in range(M):
+                exact = sum(Fraction(float(xf[m, k])) * wh[k] for k in range(K))
+                tabs = sum(abs(Fraction(float(xf[m, k])) * wh[k]) for k in range(K))
+                assert abs(Fraction(float(y[b, m, n])) - exact) <= K * Fraction(2) ** -52 * tabs
