@@ -32,6 +32,7 @@ EXPORTS = (
     "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
+    "qmm_small_m_batched",
 )
 
 
@@ -64,6 +65,7 @@ def _load():
         "qmm_small_m_split_forced": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp,
                                            i32, i32]),
         "qmm_split_plan": (i32, [i32, i32, i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "qmm_small_m_batched": (i32, [i32, i32, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -88,6 +90,7 @@ qmm_small_m_ws = _lib.qmm_small_m_ws
 qmm_small_m_workspace_bytes = _lib.qmm_small_m_workspace_bytes
 qmm_small_m_split_forced = _lib.qmm_small_m_split_forced
 qmm_split_plan = _lib.qmm_split_plan
+qmm_small_m_batched = _lib.qmm_small_m_batched
 
 
 def strerror(status: int) -> str:
@@ -203,6 +206,26 @@ def small_m(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: tor
         _check(qmm_small_m(*args), "qmm_small_m")
     else:
         _check(qmm_small_m_forced(*args, int(kernel)), "qmm_small_m_forced")
+    return out
+
+
+def small_m_batched(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+                    group_size: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [B, M, N]: y[b] = x[b] . dequant(wq[b], scales[b], biases[b])^T, one weight set per entry
+    (x [B, M, K], wq [B, N, words], scales / biases [B, N, K/gs])."""
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    B, M, K = x.shape
+    N = wq.shape[1]
+    if wq.shape[0] != B or scales.shape[0] != B or biases.shape[0] != B:
+        raise ValueError("x, wq, scales and biases need the same batch size")
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(qmm_small_m_batched(_dt(x.dtype), bits, group_size, B, M, N, K, x.data_ptr(), wq.data_ptr(),
+                               scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
+           "qmm_small_m_batched")
     return out
 
 

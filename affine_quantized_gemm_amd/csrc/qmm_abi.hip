@@ -6,6 +6,8 @@
 // ("What Are NAX Verify Kernels and When Is the Turbo Profile Activated in
 // MTPLX?", "Frequently Asked Questions"); this library has one code path per
 // variant and reports QMM_ERR_UNSUPPORTED instead.
+#include <algorithm>
+#include <cstdint>
 #include <stdint.h>
 
 #include <initializer_list>
@@ -111,6 +113,37 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
     const int kid = qmm::select_kernel(dt, bits, group_size, M, N, K);
     qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream)};
     return hip_status(qmm::launch_kernel(kid, a));
+}
+
+int qmm_small_m_batched(int dt, int bits, int group_size, int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const void* x, const uint32_t* wq, const void* scales, const void* biases, void* y,
+                        void* stream) {
+    if (batch < 0 || M < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, N, K);
+    if (st != QMM_OK) return st;
+    if (M > 64) return QMM_ERR_UNSUPPORTED;
+    if (batch == 0 || M == 0 || N == 0) return QMM_OK;
+    st = check_ptrs({x, wq, scales, biases, y});
+    if (st != QMM_OK) return st;
+    // bytes of one entry's array; every entry starts 16-byte aligned
+    const int64_t sx = M * K * 2, sw = N * (K * bits / 8), ss = N * (K / group_size) * 2, sy = M * N * 2;
+    const int64_t smax = std::max(std::max(sx, sw), std::max(ss, sy));
+    if (batch > INT64_MAX / smax) return QMM_ERR_INVALID_ARG;
+    if (batch > 1 && ((sx | sw | ss | sy) & 15) != 0) return QMM_ERR_MISALIGNED;
+    const int kid = qmm::select_kernel(dt, bits, group_size, M, N, K);
+    auto at = [](const void* p, int64_t off) { return static_cast<const void*>(static_cast<const char*>(p) + off); };
+    // the register kernel takes up to 65535 entries per launch (grid.y); the
+    // others one launch per entry
+    const int64_t per = kid == QMM_KERNEL_MFMA_REG ? 65535 : 1;
+    for (int64_t b0 = 0; b0 < batch; b0 += per) {
+        qmm::MatmulArgs a{dt, bits, group_size, M, N, K, at(x, b0 * sx),
+                          static_cast<const uint32_t*>(at(wq, b0 * sw)), at(scales, b0 * ss), at(biases, b0 * ss),
+                          const_cast<void*>(at(y, b0 * sy)), static_cast<hipStream_t>(stream)};
+        a.batch = std::min(per, batch - b0);
+        st = hip_status(qmm::launch_kernel(kid, a));
+        if (st != QMM_OK) return st;
+    }
+    return QMM_OK;
 }
 
 int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int* kernel_id, int* split) {

@@ -26,6 +26,10 @@ struct MatmulArgs {
     // split < 2: no split, `part` unused.
     float* part;
     int split;
+    // Batch entries (register kernel only; the others are launched once per
+    // entry): entry b reads x, wq, scales, biases and writes y at b times the
+    // dense size of one entry's array.
+    int64_t batch = 1;
 };
 
 hipError_t launch_valu(const MatmulArgs& a);

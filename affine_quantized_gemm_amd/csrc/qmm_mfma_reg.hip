@@ -236,6 +236,15 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     static_assert(!ROWS || ((reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>() || !MULTI) && !MH),
                   "row blocks run the LDS-ring form or one tile per workgroup, all 16 rows");
     const int m_all = M;  // rows of x and y (of each partial output when split)
+    if constexpr (!SPLIT) {
+        // batch entry blockIdx.y: dense [batch][...] arrays
+        const int64_t be = blockIdx.y;
+        x += be * m_all * K;
+        wq += be * N * (K * BITS / 32);
+        scales += be * N * (K / GS);
+        biases += be * N * (K / GS);
+        y += be * m_all * N;
+    }
     int r0 = 0;           // first row of this workgroup's block
     if constexpr (ROWS) {
         r0 = 16 * static_cast<int>(blockIdx.z);
@@ -840,11 +849,27 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
     const int64_t ntiles = (a.N + 15) / 16;
-    const int64_t grid = SPLIT  ? 256 * (16 / W) / (S * RB)
-                         : ROWS ? (MULTI ? reg_rows_grid(RB) : ntiles)
-                                : reg_grid(ntiles, W);
-    if (ROWS && (a.M <= 16 || a.M > 64 || (MULTI ? ntiles <= grid : ntiles > reg_grid(ntiles, W))))
+    // batch entries (grid.y, unsplit) share the resident workgroups of a
+    // multi-tile grid
+    const int64_t nb = SPLIT ? 1 : a.batch;
+    int64_t grid = SPLIT  ? 256 * (16 / W) / (S * RB)
+                   : ROWS ? (MULTI ? reg_rows_grid(RB) : ntiles)
+                          : reg_grid(ntiles, W);
+    if (MULTI && !SPLIT && nb > 1) {
+        if (ROWS) {
+            grid = reg_rows_grid(RB) / nb / 8 * 8;  // (row blocks of a slot on one XCD)
+            if (grid < 8) grid = 8;
+        } else {
+            grid = 256 * (16 / W) / nb;
+            if (grid < 1) grid = 1;
+            if (grid > ntiles) grid = ntiles;
+        }
+    }
+    if (MULTI && a.N < 16) return hipErrorInvalidValue;  // (the shifted last tile)
+    if (ROWS && (a.M <= 16 || a.M > 64 ||
+                 (MULTI ? ntiles <= reg_rows_grid(RB) : ntiles > reg_grid(ntiles, W))))
         return hipErrorInvalidValue;
+    if (nb < 1 || nb > 65535 || (SPLIT && a.batch != 1)) return hipErrorInvalidValue;
     if (MH && a.M > 8) return hipErrorInvalidValue;  // partial tiles keep rows 0..7 only
     if (SPLIT && (grid < 1 || S < 2 || kr * S != a.K || a.part == nullptr)) return hipErrorInvalidValue;
     const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(ROWS ? 16 : a.M, kr);
@@ -857,7 +882,8 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
         if (attr != hipSuccess) return attr;
     }
     hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
-                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(S), static_cast<unsigned>(RB)),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(SPLIT ? S : nb),
+                            static_cast<unsigned>(RB)),
                        dim3(64 * W), lds, a.stream,
                        static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
                        static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M), a.N,
@@ -869,7 +895,10 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
 
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC>
 hipError_t launch_shape(const MatmulArgs& a) {
-    const int64_t ntiles = (a.N + 15) / 16;
+    // the tiles of every batch entry against the resident workgroups (the
+    // multi-tile forms shift a ragged last tile back to end at column N, so
+    // entries narrower than a tile stay single-tile)
+    const int64_t ntiles = (a.N + 15) / 16 * (a.N >= 16 ? a.batch : 1);
     if (ntiles > reg_grid(ntiles, W)) {
         // 8-bit vector form at M <= 8: weights through LDS (partial tiles of
         // rows 0..7) where that fits in LDS (not gs32 at K = 4096); otherwise

@@ -168,6 +168,54 @@ def layer_table(rows):
     return out
 
 
+# (shape, batch entries, M) timed with --batched
+BATCHED = (("kv", 8, 1), ("kv", 8, 6), ("kv", 8, 32), ("kv", 32, 4), ("verify", 4, 6), ("verify8", 4, 6), ("gateup", 2, 6))
+
+
+def sweep_batched(stack_mib):
+    """qmm_small_m_batched against one qmm_small_m call per entry, over a
+    stack of batched weight sets larger than the caches (graph-replayed)."""
+    rows = []
+    for name, nb, M in BATCHED:
+        N, K, dt, bits, gs = SHAPES[name]
+        tdt = synth.TORCH_DT[dt]
+        Bw = nb * weight_bytes(N, K, bits, gs)
+        S = max(2, -(-(stack_mib << 20) // Bw))
+        stack = []
+        for i in range(S):
+            ents = []
+            for b in range(nb):
+                w = synth.normal((N, K), 0.02, dt, 7000 + nb * i + b, device="cuda")
+                ents.append(Q.quantize(w, bits, gs))
+                del w
+            stack.append(tuple(torch.stack([e[j] for e in ents]) for j in range(3)))
+            del ents
+        x = synth.normal((nb, M, K), 1.0, dt, 7600 + M, device="cuda")
+        y = torch.empty((nb, M, N), dtype=tdt, device="cuda")
+
+        def run_batched():
+            for (wq, sc, bi) in stack:
+                Q.small_m_batched(x, wq, sc, bi, bits, gs, out=y)
+
+        def run_each():
+            for (wq, sc, bi) in stack:
+                for b in range(nb):
+                    Q.small_m(x[b], wq[b], sc[b], bi[b], bits, gs, out=y[b])
+
+        tb = round(time_calls(run_batched, len(stack)), 3)
+        te = round(time_calls(run_each, len(stack)), 3)
+        sel = Q.kernel_name(Q.select_kernel(tdt, bits, gs, M, N, K))
+        row = {"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "batch": nb, "M": M,
+               "kernel": sel, "batched_us": tb, "per_entry_calls_us": te,
+               "batched_gbs": round(Bw / (tb * 1e-6) / 1e9, 1)}
+        rows.append(row)
+        print(f"batched {name:8s} B={nb} M={M:3d}  {sel}  one batched call {tb:8.2f} us ({row['batched_gbs']} GB/s)"
+              f"   {nb} calls {te:8.2f} us", flush=True)
+        del stack
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--shapes", default=",".join(SHAPES))
@@ -176,9 +224,10 @@ def main():
     p.add_argument("--json", default=None)
     p.add_argument("--splits", action="store_true", help="also time K splits (workspace path)")
     p.add_argument("--layer", action="store_true", help="also sum one decoder layer's projections per M")
+    p.add_argument("--batched", action="store_true", help="also time the batched entry point")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
-    shapes = a.shapes.split(",")
+    shapes = [s for s in a.shapes.split(",") if s]
     if a.layer:
         shapes += [name for name, _ in LAYER if name not in shapes]
     rows = []
@@ -191,6 +240,10 @@ def main():
             print(f"layer  M={t['M']:3d}  {t['layer_us']:8.2f} us  (with the workspace plan {t['layer_ws_us']:8.2f} us)",
                   flush=True)
         out = {"rows": rows, "layer": table}
+    if a.batched:
+        brows = sweep_batched(a.stack_mib)
+        out = dict(out) if isinstance(out, dict) else {"rows": rows}
+        out["batched"] = brows
     if a.json:
         with open(a.json, "w") as f:
             json.dump(out, f, indent=1)

@@ -114,6 +114,27 @@ int qmm_small_m(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t 
                 const void* x, const uint32_t* wq, const void* scales,
                 const void* biases, void* y, void* stream);
 
+/*
+ * Batched form: `batch` independent products, each with its own weights,
+ *   y[b] [M, N] = x[b] [M, K] . dequant(wq[b], scales[b], biases[b])^T,
+ * over dense arrays x [batch, M, K], wq [batch, N, K*bits/32],
+ * scales / biases [batch, N, K/gs], y [batch, M, N] (entry b at b times one
+ * entry's size).  MLX issue #4720, "Describe the bug", confines its dispatch
+ * story to transposed, non-batched calls; this is the batched case of the
+ * same product.  The variant is the one qmm_small_m picks for (M, N, K);
+ * the register-resident variant runs every entry in one launch (entries
+ * share its resident workgroups), the others launch once per entry.  Each
+ * entry's result is bit-identical to qmm_small_m on that entry.
+ * batch < 0 -> QMM_ERR_INVALID_ARG; batch == 0 (or M == 0 or N == 0) ->
+ * QMM_OK with nothing launched (NULL allowed); with batch > 1 every entry's
+ * arrays must start 16-byte aligned (M*K*2, N*K*bits/8, N*(K/gs)*2 and
+ * M*N*2 bytes multiples of 16), else QMM_ERR_MISALIGNED.  Otherwise as
+ * qmm_small_m.
+ */
+int qmm_small_m_batched(int dt, int bits, int group_size, int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const void* x, const uint32_t* wq, const void* scales, const void* biases,
+                        void* y, void* stream);
+
 /* As qmm_small_m with the variant forced (measurement and tests).
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
  * (QMM_KERNEL_MFMA_REG needs K <= 4096; for M = 17..64 it runs on 16-row

@@ -270,3 +270,28 @@ def test_split_entry_validation():
         Q.QMM_ERR_INVALID_ARG
     # empty problems: OK, nothing launched
     assert Q.qmm_small_m_ws(f16, 4, 64, 0, 4096, 14336, None, None, None, None, None, None, 0, None) == Q.QMM_OK
+
+
+def test_batched_validation():
+    """qmm_small_m_batched: errors before any HIP call (fake addresses, no GPU)."""
+    bm = Q.qmm_small_m_batched
+    ok = (0, 4, 64, 3, 4, 64, 256)  # dt, bits, gs, batch, M, N, K
+    ptrs = (A, A, A, A, A, None)
+    assert bm(0, 4, 64, -1, 4, 64, 256, *ptrs) == Q.QMM_ERR_INVALID_ARG
+    assert bm(0, 4, 64, 2, -1, 64, 256, *ptrs) == Q.QMM_ERR_INVALID_ARG
+    assert bm(0, 5, 64, 2, 4, 64, 256, *ptrs) == Q.QMM_ERR_UNSUPPORTED
+    assert bm(0, 4, 64, 2, 65, 64, 256, *ptrs) == Q.QMM_ERR_UNSUPPORTED
+    assert bm(*ok, None, A, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
+    assert bm(*ok, A, A, A, A, MIS, None) == Q.QMM_ERR_MISALIGNED
+    # entries that would not start 16-byte aligned: y of one entry is 3 x 17 x 2 bytes
+    assert bm(0, 4, 64, 2, 3, 17, 256, *ptrs) == Q.QMM_ERR_MISALIGNED
+    # scale rows of one entry: 17 rows x 3 groups x 2 bytes
+    assert bm(0, 4, 64, 2, 8, 17, 192, *ptrs) == Q.QMM_ERR_MISALIGNED
+    # ... which a single entry does not need
+    assert bm(0, 4, 64, 1, 3, 17, 256, None, A, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
+    # empty problems: OK with nothing launched, NULL allowed
+    assert bm(0, 4, 64, 0, 4, 64, 256, None, None, None, None, None, None) == Q.QMM_OK
+    assert bm(0, 4, 64, 3, 0, 64, 256, None, None, None, None, None, None) == Q.QMM_OK
+    assert bm(1, 8, 32, 3, 4, 0, 256, None, None, None, None, None, None) == Q.QMM_OK
+    # byte offsets that overflow int64
+    assert bm(0, 8, 32, 2 ** 62, 64, 4096, 4096, *ptrs) == Q.QMM_ERR_INVALID_ARG

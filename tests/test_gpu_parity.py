@@ -344,6 +344,43 @@ def test_reg_row_blocks_single_tile(Q, dt, bits, gs, K, N):
             assert torch.equal(y[r0:r0 + 16].view(torch.int16), yb.view(torch.int16)), (M, r0)
 
 
+@pytest.mark.parametrize("dt,bits,gs,B,M,N,K", [
+    ("f16", 4, 64, 4, 6, 1024, 4096),          # register kernel, one tile per workgroup, one launch
+    ("bf16", 4, 64, 3, 24, 1000, 2048),        # ... on 16-row blocks, ragged N
+    ("bf16", 4, 64, 2, 8, 16 * 300 + 5, 4096),  # LDS ring, entries sharing the resident workgroups
+    ("f16", 8, 64, 3, 12, 16 * 270, 4096),     # 8-bit register prefetch, several tiles per workgroup
+    ("f16", 4, 64, 3, 36, 16 * 300, 4096),     # LDS ring on row blocks
+    ("f16", 4, 64, 3, 8, 256, 14336),          # pass kernel: a launch per entry
+    ("bf16", 6, 128, 2, 40, 8192, 4096),       # 64-column tile kernel: a launch per entry
+    ("f16", 4, 64, 100, 4, 40, 4096),          # many small entries: LDS ring over 3 ragged tiles each
+    ("bf16", 8, 64, 6, 6, 1024, 4096),         # 8-bit, entries' tiles beyond the resident workgroups
+    ("f16", 4, 64, 300, 4, 8, 2048),           # entries narrower than a tile: one tile each
+])
+def test_batched(Q, dt, bits, gs, B, M, N, K):
+    """qmm_small_m_batched: every entry against the oracle's batched product
+    and bit-identical to qmm_small_m on that entry alone."""
+    print(f"batched {dt} {bits}-bit gs{gs} B={B} M={M} N={N} K={K} "
+          f"kernel={Q.kernel_name(Q.select_kernel(DT[dt], bits, gs, M, N, K))}", flush=True)
+    xs, qs = [], []
+    for b in range(B):
+        w = synth.normal((N, K), 0.02, dt, 9000 + 10 * b + bits)
+        qs.append(oracle_quant(w, dt, bits, gs))
+        xs.append(synth.to_oracle(synth.normal((M, K), 1.0, dt, 9100 + 10 * b + M)))
+    owq, osc, obi = (np.stack([q[i] for q in qs]) for i in range(3))
+    ox = np.stack(xs)
+    x = synth.from_oracle(ox, dt).cuda()
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    y = Q.small_m_batched(x, wq, sc, bi, bits, gs)
+    torch.cuda.synchronize()
+    assert y.shape == (B, M, N)
+    yo, T = O.qmm_batched(ox, owq, osc, obi, dt, bits, gs)
+    ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+    assert ok, worst
+    for b in range(B):
+        yb = Q.small_m(x[b], wq[b], sc[b], bi[b], bits, gs)
+        assert torch.equal(y[b].view(torch.int16), yb.view(torch.int16)), b
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
