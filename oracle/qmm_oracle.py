@@ -20,6 +20,8 @@ What it computes (sources are the web pages this project is built from):
 * The batched form, one weight matrix per batch entry (the adjacent API
   case to the transposed, non-batched call of MLX issue #4720, "Describe the
   bug").
+* The non-transposed product y = x . dequant(W) with W stored [K, N] and
+  quantized along N (the other orientation of the same call).
 * Weight bytes per call = packed words + 4 bytes of scale/bias per group --
   MLX issue #4720, "To Reproduce" (the ``wbytes`` expression).
 
@@ -273,6 +275,22 @@ def qmm_batched(x, wq, scales, biases, dt: str, bits: int, group_size: int):
     for b in range(B):
         y[b], T[b] = qmm(x[b], wq[b], scales[b], biases[b], dt, bits, group_size)
     return y, T
+
+
+def qmm_nt(x, wq, scales, biases, dt: str, bits: int, group_size: int, N: int):
+    """Non-transposed product y = x . dequant(W) with W stored [K, N].
+
+    MLX issue #4720, "Describe the bug", concerns calls with transposed
+    weights; the other orientation (``transpose=False``) keeps W as [K, N],
+    quantized along its last axis: row k of W is packed and grouped along N
+    exactly as a row of the transposed layout is along K (``wq`` [K, N*bits/32],
+    ``scales`` and ``biases`` [K, N/gs]).  x is [M, K].  Returns
+    (y [M, N], T [M, N]) with T[m, n] = sum_k |x[m, k]| |w_hat[k, n]|, fp64,
+    unrounded, as :func:`qmm`.
+    """
+    x64 = to_f64(x, dt)
+    w64 = dequantize_exact(wq, scales, biases, dt, bits, group_size, N)  # [K, N]
+    return x64 @ w64, np.abs(x64) @ np.abs(w64)
 
 
 def qmm_columns(x, wq, scales, biases, dt: str, bits: int, group_size: int, cols):

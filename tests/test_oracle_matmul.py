@@ -165,3 +165,71 @@ def test_batched_exact_rationals():
                 exact = sum(Fraction(float(xf[m, k])) * wh[k] for k in range(K))
                 tabs = sum(abs(Fraction(float(xf[m, k])) * wh[k]) for k in range(K))
                 assert abs(Fraction(float(y[b, m, n])) - exact) <= K * Fraction(2) ** -52 * tabs
+
+
+# ---------------------------------------------------------------------------
+# non-transposed form: W stored [K, N], quantized along N
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 4, 32), ("bf16", 6, 64), ("bf16", 8, 128)])
+def test_nt_exact_rationals(dt, bits, gs):
+    """Tiny non-transposed products against exact rational sums, with an
+    independent big-integer unpack of each row k of W [K, N]."""
+    M, K, N = 2, 3, 2 * gs
+    w = synth.to_oracle(synth.normal((K, N), 0.02, dt, 101))
+    x = synth.to_oracle(synth.normal((M, K), 1.0, dt, 102))
+    wq, sc, bi = O.quantize(w, dt, bits, gs)
+    assert wq.shape[0] == K and sc.shape == (K, N // gs)
+    y, T = O.qmm_nt(x, wq, sc, bi, dt, bits, gs, N)
+    assert y.shape == (M, N)
+    xf, s, b = O.to_f64(x, dt), O.to_f64(sc, dt), O.to_f64(bi, dt)
+    rows = [bigint_unpack_row(wq[k], bits, N) for k in range(K)]
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(float(xf[m, k])) * (Fraction(float(s[k, n // gs])) * rows[k][n]
+                                                   + Fraction(float(b[k, n // gs]))) for k in range(K)]
+            exact, tabs = sum(terms), sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[m, n])) - exact) <= K * Fraction(2) ** -52 * tabs
+            assert abs(Fraction(float(T[m, n])) - tabs) <= K * Fraction(2) ** -52 * tabs
+
+
+def test_nt_one_hot_rows_recover_weight_rows():
+    """x = e_k picks row k of the dequantized [K, N] weights, which is the
+    dequantizer's output for that row (exact in fp64, then rounded once)."""
+    dt, bits, gs = "f16", 4, 64
+    K, N = 24, 192
+    w = synth.to_oracle(synth.normal((K, N), 0.02, dt, 111))
+    wq, sc, bi = O.quantize(w, dt, bits, gs)
+    x = np.zeros((K, K), np.float16)
+    x[np.arange(K), np.arange(K)] = 1
+    y, _ = O.qmm_nt(x, wq, sc, bi, dt, bits, gs, N)
+    d = O.dequantize(wq, sc, bi, dt, bits, gs, N)  # [K, N] in the dtype
+    assert np.array_equal(O.f32_to_dt_rne(y.astype(np.float32), dt).view(np.uint16), d.view(np.uint16))
+
+
+def test_nt_against_transposed_product_of_the_transpose():
+    """With the dequantized weights in hand, x . W_hat equals the transposed
+    product against W_hat^T: quantizing W_hat^T [N, K] along K with one group
+    per row segment reproduces the same values when every group of W_hat^T
+    is built from values that are already on a grid.  Here: W chosen so that
+    each [K, N] group holds exactly the values s*q + b of an integer grid,
+    and groups along both axes coincide (gs = K = N)."""
+    dt, bits, gs = "f16", 8, 64
+    K = N = 64
+    rng = np.random.default_rng(5)
+    # one scale and bias for the whole matrix: every row and column group
+    # quantizes back to the same grid, whichever axis it runs along
+    q = rng.integers(0, 256, size=(K, N))
+    q[:, 0], q[:, 1] = 0, 255  # each row reaches both ends of the grid
+    q[0, :], q[1, :] = 0, 255  # ... and each column
+    q[0, 1] = q[1, 0] = 0
+    q[1, 1] = q[0, 0] = 255
+    s, b = np.float16(2.0 ** -10), np.float16(-0.125)
+    w = (np.float16(s) * q.astype(np.float16) + b).astype(np.float16)
+    x = synth.to_oracle(synth.normal((3, K), 1.0, dt, 121))
+    wq, sc, bi = O.quantize(w, dt, bits, gs)
+    wqt, sct, bit = O.quantize(np.ascontiguousarray(w.T), dt, bits, gs)
+    y_nt, _ = O.qmm_nt(x, wq, sc, bi, dt, bits, gs, N)
+    y_t, _ = O.qmm(x, wqt, sct, bit, dt, bits, gs)
+    assert np.allclose(y_nt, y_t, rtol=1e-12, atol=1e-12)
+    assert np.allclose(y_nt, O.to_f64(x, dt) @ w.astype(np.float64), rtol=1e-12, atol=1e-12)
