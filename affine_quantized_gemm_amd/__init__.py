@@ -32,7 +32,7 @@ EXPORTS = (
     "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
-    "qmm_small_m_batched",
+    "qmm_small_m_batched", "qmm_small_m_nt",
 )
 
 
@@ -66,6 +66,7 @@ def _load():
                                            i32, i32]),
         "qmm_split_plan": (i32, [i32, i32, i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "qmm_small_m_batched": (i32, [i32, i32, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "qmm_small_m_nt": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -91,6 +92,7 @@ qmm_small_m_workspace_bytes = _lib.qmm_small_m_workspace_bytes
 qmm_small_m_split_forced = _lib.qmm_small_m_split_forced
 qmm_split_plan = _lib.qmm_split_plan
 qmm_small_m_batched = _lib.qmm_small_m_batched
+qmm_small_m_nt = _lib.qmm_small_m_nt
 
 
 def strerror(status: int) -> str:
@@ -226,6 +228,26 @@ def small_m_batched(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, bia
     _check(qmm_small_m_batched(_dt(x.dtype), bits, group_size, B, M, N, K, x.data_ptr(), wq.data_ptr(),
                                scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
            "qmm_small_m_batched")
+    return out
+
+
+def small_m_nt(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+               group_size: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] . dequant(W) for W stored [K, N] and quantized along N
+    (wq [K, N*bits/32], scales / biases [K, N/gs]: :func:`quantize` of a [K, N] matrix)."""
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    M, K = x.shape
+    if wq.shape[0] != K:
+        raise ValueError("wq needs one row per column of x")
+    N = wq.shape[1] * 32 // bits
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(qmm_small_m_nt(_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(),
+                          scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
+           "qmm_small_m_nt")
     return out
 
 

@@ -146,6 +146,20 @@ int qmm_small_m_batched(int dt, int bits, int group_size, int64_t batch, int64_t
     return QMM_OK;
 }
 
+int qmm_small_m_nt(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                   const uint32_t* wq, const void* scales, const void* biases, void* y, void* stream) {
+    if (M < 0 || K < 0) return QMM_ERR_INVALID_ARG;
+    // the quantized axis is N here: it obeys the rules K obeys in the transposed layout
+    int st = check_format(dt, bits, group_size, K, N);
+    if (st != QMM_OK) return st;
+    if (M > 64 || K < 32 || K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (M == 0) return QMM_OK;
+    st = check_ptrs({x, wq, scales, biases, y});
+    if (st != QMM_OK) return st;
+    qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream)};
+    return hip_status(qmm::launch_nt(a));
+}
+
 int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int* kernel_id, int* split) {
     if (M < 0 || kernel_id == nullptr || split == nullptr) return QMM_ERR_INVALID_ARG;
     int st = check_format(dt, bits, group_size, N, K);

@@ -38,6 +38,8 @@ hipError_t launch_mfma_pass(const MatmulArgs& a);
 // tile kernel shapes (columns per workgroup tile)
 enum { TILE_CFG_16 = 0, TILE_CFG_64 = 1 };
 hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg);
+// non-transposed weights (W [K, N], quantized along N): y = x . dequant(W)
+hipError_t launch_nt(const MatmulArgs& a);
 // M <= 16: every format where the k-blocks fit; M 17..64, on 16-row blocks
 // (vector form, 16 wavefronts): 4-bit LDS-ring grids on shapes with more
 // 16-column tiles than column slots, else any width where 16 rows take one

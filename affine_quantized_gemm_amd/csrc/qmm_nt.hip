@@ -1,0 +1,252 @@
+// Non-transposed product: y[M, N] = x[M, K] . dequant(W)[K, N], with W
+// stored [K, N] and quantized along N -- row k of W is a packed bitstream of
+// N codes with one scale and bias per group of gs consecutive columns
+// (scales, biases [K, N/gs]).  This is the other orientation of the call in
+// MLX issue #4720, "Describe the bug" (there: transposed weights).
+//
+// Here the reduction runs down the rows of W, so a column's codes are not
+// contiguous.  One workgroup owns 16 output columns (inside one group, since
+// gs >= 32) for all of K; its 16 wavefronts take 32-row steps in turn:
+//   * a lane loads the 8 codes of row k0 + l/2, columns 8 (l % 2) .. + 8
+//     (4 / 6 / 8 bytes), and widens them to bytes;
+//   * an 8 x 8 byte transpose among the 8 lanes of equal (l / 16, l % 2)
+//     (three swizzle-and-merge stages, no LDS) leaves lane l with the codes
+//     of rows k0 + 8 (l / 16) .. + 8 of one column: the MFMA B operand.  The
+//     column a lane holds is c(p) = 8 (p % 2) + p / 2 for p = l % 16, a fixed
+//     relabeling undone at the store;
+//   * the scale multiplies the activations: A = x[m, k] s[k, g] in fp32,
+//     split into dt parts hi + lo (hi = RNE(A), lo = RNE(A - hi)), so that
+//     the codes (exact small integers in dt) meet x s with a relative error
+//     of about u^2; the bias adds sum_k x[m, k] b[k, g] through one more
+//     matrix step with a B operand whose 16 columns all hold b[k, g];
+//   * partial 16 x 16 tiles of the wavefronts are added through LDS and
+//     rounded once.
+// The scales and biases of the workgroup's group are staged in LDS for up
+// to 4096 rows at a time.  Column blocks that share 128-byte weight lines
+// run on one XCD (block ids congruent mod 8), so the lines come from HBM once.
+#include "qmm.h"
+#include "qmm_internal.hpp"
+#include "qmm_mfma_frag.hpp"
+
+namespace qmm {
+namespace {
+
+using mf::Frag;
+using mf::float4_t;
+
+constexpr int NT_W = 16;     // wavefronts per workgroup
+constexpr int NT_KC = 4096;  // rows of scales and biases staged at a time
+
+// partner value for the transpose: lane l ^ D (D < 32)
+template <int D>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), (D << 10) | 0x1F));
+}
+
+// The 8 codes of this lane's row and column half, as bytes (lo: columns
+// 0..3, hi: 4..7 of the half).
+template <int BITS>
+__device__ __forceinline__ void load_codes(const uint32_t* __restrict__ row, int64_t n0, int h, uint32_t& lo,
+                                           uint32_t& hi) {
+    if constexpr (BITS == 4) {
+        const uint32_t w = row[n0 / 8 + h];
+        auto spread = [](uint32_t t) {  // 4 nibbles -> 4 bytes
+            return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
+        };
+        lo = spread(w & 0xFFFFu);
+        hi = spread(w >> 16);
+    } else if constexpr (BITS == 8) {
+        lo = row[n0 / 4 + 2 * h];
+        hi = row[n0 / 4 + 2 * h + 1];
+    } else {
+        // 16 columns = 3 words; this half's 48 bits start at bit 48 h
+        const int64_t base = n0 / 16 * 3 + h;
+        const uint64_t u = (static_cast<uint64_t>(row[base + 1]) << 32 | row[base]) >> (16 * h);
+        uint32_t b[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) b[c] = static_cast<uint32_t>(u >> (6 * c)) & 63u;
+        lo = b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24;
+        hi = b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24;
+    }
+}
+
+// one merge stage of the transpose on one word: lanes whose row bit is
+// clear keep their low part and take the partner's low part shifted up;
+// the others take the partner's high part shifted down and keep their own
+template <int LANE_DIST, uint32_t MASK, int SHIFT>
+__device__ __forceinline__ uint32_t merge(uint32_t v, bool upper) {
+    const uint32_t p = xor_lane<LANE_DIST>(v);
+    return upper ? ((p >> SHIFT) & MASK) | (v & ~MASK) : (v & MASK) | ((p & MASK) << SHIFT);
+}
+
+// 8 codes (bytes) -> an MFMA operand of 8 exact dt values
+template <int DT>
+__device__ __forceinline__ Frag codes_frag(uint32_t lo, uint32_t hi) {
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = i < 2 ? lo : hi;
+        const int b0 = 2 * (i & 1);
+        const float a = static_cast<float>((w >> (8 * b0)) & 0xFFu);
+        const float b = static_cast<float>((w >> (8 * b0 + 8)) & 0xFFu);
+        if constexpr (DT == DT_F16) {
+            f.v[i] = static_cast<uint32_t>(DtOps<DT>::rne(a)) | static_cast<uint32_t>(DtOps<DT>::rne(b)) << 16;
+        } else {  // integers below 256 are exact in bf16: the top half of the fp32 pattern
+            f.v[i] = (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
+        }
+    }
+    return f;
+}
+
+template <int DT, int BITS, int RB>
+__global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __restrict__ x,
+                                                          const uint32_t* __restrict__ wq,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ biases,
+                                                          uint16_t* __restrict__ y, int M, int64_t N, int64_t K,
+                                                          int gs) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint16_t* const s_lds = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* const b_lds = s_lds + NT_KC;
+    float* const red = reinterpret_cast<float*>(lds);  // (after the last step)
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nblk = static_cast<int>(N / 16);
+    // column blocks sharing weight lines on one XCD
+    const int bid = static_cast<int>(blockIdx.x);
+    const int cb = nblk % 8 == 0 ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+    const int64_t n0 = 16 * static_cast<int64_t>(cb);
+    const int64_t G = N / gs;
+    const int64_t g = n0 / gs;
+    const int64_t row_words = N * BITS / 32;
+
+    const int h = lane & 1;           // column half of this lane's load
+    const int kk = lane >> 1;         // row of this lane's load in the step
+    const int r = kk & 7;             // its row inside the 8 x 8 transpose
+    const int p = lane & 15;          // MFMA column slot (column c(p))
+    const int jq = lane >> 4;         // k-slot quarter / D row quarter
+
+    float4_t acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[b] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int64_t kc0 = 0; kc0 < K; kc0 += NT_KC) {
+        const int kc = static_cast<int>(K - kc0 < NT_KC ? K - kc0 : NT_KC);
+        for (int t = threadIdx.x; t < kc; t += 64 * NT_W) {
+            s_lds[t] = scales[(kc0 + t) * G + g];
+            b_lds[t] = biases[(kc0 + t) * G + g];
+        }
+        __syncthreads();
+        for (int step = wave; step < kc / 32; step += NT_W) {
+            const int64_t k0 = kc0 + 32 * static_cast<int64_t>(step);
+            uint32_t lo, hi;
+            load_codes<BITS>(wq + (k0 + kk) * row_words, n0, h, lo, hi);
+            // rows r, r ^ 4 (lanes 8 apart): swap the 4-column halves
+            {
+                const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
+                if (r & 4) lo = phi;
+                else hi = plo;
+            }
+            lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
+            hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
+            lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
+            hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+            const Frag qf = codes_frag<DT>(lo, hi);
+            // this lane's 8 rows: scales and biases
+            const int kl = static_cast<int>(k0 - kc0) + 8 * jq;
+            const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + kl);
+            const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + kl);
+            Frag bf;
+            bf.v[0] = bv.x; bf.v[1] = bv.y; bf.v[2] = bv.z; bf.v[3] = bv.w;
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int m = 16 * b + p;
+                uint4 xv = make_uint4(0u, 0u, 0u, 0u);
+                if (m < M) xv = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K + k0 + 8 * jq);
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+                Frag xf, ah, al;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xf.v[i] = xw[i];
+                    uint32_t hh = 0, ll = 0;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float a = DtOps<DT>::to_f32(static_cast<uint16_t>(xw[i] >> (16 * e))) *
+                                        DtOps<DT>::to_f32(static_cast<uint16_t>(sw[i] >> (16 * e)));
+                        const uint16_t ahi = DtOps<DT>::rne(a);
+                        const uint16_t alo = DtOps<DT>::rne(a - DtOps<DT>::to_f32(ahi));
+                        hh |= static_cast<uint32_t>(ahi) << (16 * e);
+                        ll |= static_cast<uint32_t>(alo) << (16 * e);
+                    }
+                    ah.v[i] = hh;
+                    al.v[i] = ll;
+                }
+                acc[b] = mf::mfma<DT>(ah, qf, acc[b]);
+                acc[b] = mf::mfma<DT>(al, qf, acc[b]);
+                acc[b] = mf::mfma<DT>(xf, bf, acc[b]);
+            }
+        }
+        __syncthreads();  // (the staged scales are overwritten next, or the buffer reused below)
+    }
+
+    // add the wavefronts' partial tiles: red[((w RB + b) 4 + q) 64 + lane]
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[((wave * RB + b) * 4 + q) * 64 + lane] = acc[b][q];
+    __syncthreads();
+    for (int t = threadIdx.x; t < RB * 4 * 64; t += 64 * NT_W) {
+        const int ln = t & 63, q = (t >> 6) & 3, b = t >> 8;
+        float v = 0.0f;
+        for (int w = 0; w < NT_W; ++w) v += red[((w * RB + b) * 4 + q) * 64 + ln];
+        const int m = 16 * b + 4 * (ln >> 4) + q;
+        const int pp = ln & 15;
+        const int64_t n = n0 + 8 * (pp & 1) + (pp >> 1);
+        if (m < M) y[static_cast<int64_t>(m) * N + n] = DtOps<DT>::rne(v);
+    }
+}
+
+template <int DT, int BITS, int RB>
+hipError_t launch_nt_t(const MatmulArgs& a) {
+    const size_t lds_sb = 2 * NT_KC * sizeof(uint16_t);
+    const size_t lds_red = static_cast<size_t>(NT_W) * RB * 4 * 64 * sizeof(float);
+    const size_t lds = lds_sb > lds_red ? lds_sb : lds_red;
+    hipLaunchKernelGGL((nt_kernel<DT, BITS, RB>), dim3(static_cast<unsigned>(a.N / 16)), dim3(64 * NT_W), lds,
+                       a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),
+                       static_cast<const uint16_t*>(a.biases), static_cast<uint16_t*>(a.y), static_cast<int>(a.M),
+                       a.N, a.K, a.gs);
+    return hipGetLastError();
+}
+
+template <int DT, int BITS>
+hipError_t launch_nt_b(const MatmulArgs& a) {
+    switch ((a.M + 15) / 16) {
+        case 1: return launch_nt_t<DT, BITS, 1>(a);
+        case 2: return launch_nt_t<DT, BITS, 2>(a);
+        case 3: return launch_nt_t<DT, BITS, 3>(a);
+        case 4: return launch_nt_t<DT, BITS, 4>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_nt(const MatmulArgs& a) {
+    // shapes the kernel assumes (validated by the caller)
+    if (a.M < 1 || a.M > 64 || a.N < 64 || a.N % 64 != 0 || a.N % a.gs != 0 || a.gs < 32 || a.K < 32 ||
+        a.K % 32 != 0)
+        return hipErrorInvalidValue;
+    switch (a.dt * 10 + a.bits) {
+        case 4: return launch_nt_b<DT_F16, 4>(a);
+        case 6: return launch_nt_b<DT_F16, 6>(a);
+        case 8: return launch_nt_b<DT_F16, 8>(a);
+        case 14: return launch_nt_b<DT_BF16, 4>(a);
+        case 16: return launch_nt_b<DT_BF16, 6>(a);
+        case 18: return launch_nt_b<DT_BF16, 8>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qmm

@@ -216,6 +216,43 @@ def sweep_batched(stack_mib):
     return rows
 
 
+# shapes timed with --nt: the same projections with W stored [K, N]
+NT_SHAPES = ("verify", "kv", "gateup", "down")
+NT_MS = (1, 6, 16, 64)
+
+
+def sweep_nt(stack_mib):
+    """qmm_small_m_nt (W stored [K, N], quantized along N) next to the
+    transposed call on the same shape, over stacks larger than the caches."""
+    rows = []
+    for name in NT_SHAPES:
+        N, K, dt, bits, gs = SHAPES[name]
+        tdt = synth.TORCH_DT[dt]
+        B = weight_bytes(N, K, bits, gs)
+        S = max(2, -(-(stack_mib << 20) // B))
+        stack = []
+        for i in range(S):
+            w = synth.normal((K, N), 0.02, dt, 7700 + i, device="cuda")
+            stack.append(Q.quantize(w, bits, gs))
+            del w
+        for M in NT_MS:
+            x = synth.normal((M, K), 1.0, dt, 7800 + M, device="cuda")
+            y = torch.empty((M, N), dtype=tdt, device="cuda")
+
+            def run():
+                for (wq, sc, bi) in stack:
+                    Q.small_m_nt(x, wq, sc, bi, bits, gs, out=y)
+
+            t = round(time_calls(run, len(stack)), 3)
+            row = {"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "M": M, "nt_us": t,
+                   "nt_gbs": round(B / (t * 1e-6) / 1e9, 1)}
+            rows.append(row)
+            print(f"nt {name:8s} M={M:3d}  {t:8.2f} us  ({row['nt_gbs']} GB/s)", flush=True)
+        del stack
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--shapes", default=",".join(SHAPES))
@@ -225,6 +262,7 @@ def main():
     p.add_argument("--splits", action="store_true", help="also time K splits (workspace path)")
     p.add_argument("--layer", action="store_true", help="also sum one decoder layer's projections per M")
     p.add_argument("--batched", action="store_true", help="also time the batched entry point")
+    p.add_argument("--nt", action="store_true", help="also time non-transposed weights")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
     shapes = [s for s in a.shapes.split(",") if s]
@@ -244,6 +282,10 @@ def main():
         brows = sweep_batched(a.stack_mib)
         out = dict(out) if isinstance(out, dict) else {"rows": rows}
         out["batched"] = brows
+    if a.nt:
+        nrows = sweep_nt(a.stack_mib)
+        out = dict(out) if isinstance(out, dict) else {"rows": rows}
+        out["nt"] = nrows
     if a.json:
         with open(a.json, "w") as f:
             json.dump(out, f, indent=1)

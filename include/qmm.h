@@ -135,6 +135,24 @@ int qmm_small_m_batched(int dt, int bits, int group_size, int64_t batch, int64_t
                         const void* x, const uint32_t* wq, const void* scales, const void* biases,
                         void* y, void* stream);
 
+/*
+ * Non-transposed weights: y [M, N] = x [M, K] . dequant(wq, scales, biases),
+ * with W stored [K, N] and quantized along N -- the other orientation of the
+ * call in MLX issue #4720, "Describe the bug" (transposed weights there):
+ *   wq      [K, N*bits/32]  row k = the packed codes of W[k, :] (same
+ *                           bitstream as a transposed row)
+ *   scales  [K, N/gs]       one scale and bias per gs consecutive columns
+ *   biases  [K, N/gs]
+ * (what qmm_quantize produces from a [K, N] matrix).  fp32 accumulation and
+ * one rounding to dt; deterministic.  N obeys the rules K obeys in
+ * qmm_small_m (N >= 64, N % 64 == 0, N % gs == 0); K must be a positive
+ * multiple of 32; 1 <= M <= 64 (M == 0: QMM_OK, nothing launched).
+ * Otherwise as qmm_small_m.
+ */
+int qmm_small_m_nt(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                   const void* x, const uint32_t* wq, const void* scales,
+                   const void* biases, void* y, void* stream);
+
 /* As qmm_small_m with the variant forced (measurement and tests).
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
  * (QMM_KERNEL_MFMA_REG needs K <= 4096; for M = 17..64 it runs on 16-row

@@ -295,3 +295,21 @@ def test_batched_validation():
     assert bm(1, 8, 32, 3, 4, 0, 256, None, None, None, None, None, None) == Q.QMM_OK
     # byte offsets that overflow int64
     assert bm(0, 8, 32, 2 ** 62, 64, 4096, 4096, *ptrs) == Q.QMM_ERR_INVALID_ARG
+
+
+def test_nt_validation():
+    """qmm_small_m_nt: N follows the rules of the quantized axis, K a positive
+    multiple of 32; errors before any HIP call."""
+    nt = Q.qmm_small_m_nt
+    ptrs = (A, A, A, A, A, None)
+    assert nt(0, 4, 64, -1, 256, 64, *ptrs) == Q.QMM_ERR_INVALID_ARG
+    assert nt(0, 4, 64, 4, 256, -32, *ptrs) == Q.QMM_ERR_INVALID_ARG
+    assert nt(0, 4, 64, 4, 96, 64, *ptrs) == Q.QMM_ERR_UNSUPPORTED      # N % 64
+    assert nt(0, 4, 128, 4, 192, 64, *ptrs) == Q.QMM_ERR_UNSUPPORTED    # N % gs
+    assert nt(0, 4, 64, 4, 256, 48, *ptrs) == Q.QMM_ERR_UNSUPPORTED     # K % 32
+    assert nt(0, 4, 64, 4, 256, 0, *ptrs) == Q.QMM_ERR_UNSUPPORTED
+    assert nt(0, 4, 64, 65, 256, 64, *ptrs) == Q.QMM_ERR_UNSUPPORTED
+    assert nt(0, 5, 64, 4, 256, 64, *ptrs) == Q.QMM_ERR_UNSUPPORTED
+    assert nt(0, 4, 64, 4, 256, 64, A, None, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
+    assert nt(0, 4, 64, 4, 256, 64, A, A, A, MIS, A, None) == Q.QMM_ERR_MISALIGNED
+    assert nt(1, 6, 32, 0, 256, 64, None, None, None, None, None, None) == Q.QMM_OK

@@ -381,6 +381,43 @@ def test_batched(Q, dt, bits, gs, B, M, N, K):
         assert torch.equal(y[b].view(torch.int16), yb.view(torch.int16)), b
 
 
+def nt_case(Q, dt, bits, gs, M, N, K, seed, outlier=0.0):
+    """qmm_small_m_nt on W [K, N] quantized along N, against the oracle."""
+    w = synth.normal((K, N), 0.02, dt, seed, outlier_frac=outlier)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    x = synth.normal((M, K), 1.0, dt, seed + 1)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    y = Q.small_m_nt(x.cuda(), wq, sc, bi, bits, gs)
+    torch.cuda.synchronize()
+    assert y.shape == (M, N)
+    yo, T = O.qmm_nt(synth.to_oracle(x), owq, osc, obi, dt, bits, gs, N)
+    return O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T), (x.cuda(), wq, sc, bi, y)
+
+
+@pytest.mark.parametrize("dt,bits,gs", COMBOS)
+def test_nt_formats(Q, dt, bits, gs):
+    """Non-transposed weights, every format: 16-row blocks 1..4, every output."""
+    for M in (1, 6, 17, 64):
+        print(f"nt {dt} {bits}-bit gs{gs} M={M} N=256 K=96", flush=True)
+        (ok, worst), _ = nt_case(Q, dt, bits, gs, M, 256, 96, 9500 + 10 * bits + M)
+        assert ok, (M, worst)
+
+
+@pytest.mark.parametrize("dt,bits,gs,M,N,K", [
+    ("f16", 4, 64, 4, 4096, 4096),     # verify shape, weights [K, N]
+    ("bf16", 4, 64, 6, 1024, 4160),    # K past one staged chunk of scales
+    ("f16", 8, 32, 16, 64, 8192),      # one line of columns (4 blocks, not a multiple of 8)
+    ("bf16", 6, 128, 36, 384, 640),    # 24 blocks
+    ("f16", 4, 32, 64, 1024, 2048),
+])
+def test_nt_shapes(Q, dt, bits, gs, M, N, K):
+    print(f"nt {dt} {bits}-bit gs{gs} M={M} N={N} K={K}", flush=True)
+    (ok, worst), (x, wq, sc, bi, y) = nt_case(Q, dt, bits, gs, M, N, K, 9700 + M, outlier=0.01)
+    assert ok, worst
+    y2 = Q.small_m_nt(x, wq, sc, bi, bits, gs)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # deterministic
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
