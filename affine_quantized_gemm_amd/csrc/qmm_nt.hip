@@ -14,11 +14,11 @@
 //     of rows k0 + 8 (l / 16) .. + 8 of one column: the MFMA B operand.  The
 //     column a lane holds is c(p) = 8 (p % 2) + p / 2 for p = l % 16, a fixed
 //     relabeling undone at the store;
-//   * the scale multiplies the activations: A = x[m, k] s[k, g] in fp32,
-//     split into dt parts hi + lo (hi = RNE(A), lo = RNE(A - hi)), so that
-//     the codes (exact small integers in dt) meet x s with a relative error
-//     of about u^2; the bias adds sum_k x[m, k] b[k, g] through one more
-//     matrix step with a B operand whose 16 columns all hold b[k, g];
+//   * the lane dequantizes them, w = s q + b in fp32 (the scale and bias of
+//     each of its 8 rows), to the B operand hi = RNE_dt(w) -- the
+//     dequantizer's value -- and for bf16 also lo = RNE_dt(w - hi): with
+//     bf16's 8-bit significand one rounding of w and one of y could together
+//     exceed the accepted error, hi + lo carries w to about u^2;
 //   * partial 16 x 16 tiles of the wavefronts are added through LDS and
 //     rounded once.
 // The scales and biases of the workgroup's group are staged in LDS for up
@@ -79,23 +79,30 @@ __device__ __forceinline__ uint32_t merge(uint32_t v, bool upper) {
     return upper ? ((p >> SHIFT) & MASK) | (v & ~MASK) : (v & MASK) | ((p & MASK) << SHIFT);
 }
 
-// 8 codes (bytes) -> an MFMA operand of 8 exact dt values
+// 8 codes (bytes, rows e = 0..7) -> the dequantized weights w = s q + b in
+// fp32 (s, b: 8 packed dt values each), as MFMA operands: hi = RNE_dt(w)
+// (the dequantizer's value) and, for bf16, lo = RNE_dt(w - hi), so that
+// hi + lo carries w to about u^2
 template <int DT>
-__device__ __forceinline__ Frag codes_frag(uint32_t lo, uint32_t hi) {
-    Frag f;
+__device__ __forceinline__ void dequant_frags(uint32_t lo8, uint32_t hi8, const uint32_t (&sw)[4],
+                                              const uint32_t (&bw)[4], Frag& fh, Frag& fl) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t w = i < 2 ? lo : hi;
-        const int b0 = 2 * (i & 1);
-        const float a = static_cast<float>((w >> (8 * b0)) & 0xFFu);
-        const float b = static_cast<float>((w >> (8 * b0 + 8)) & 0xFFu);
-        if constexpr (DT == DT_F16) {
-            f.v[i] = static_cast<uint32_t>(DtOps<DT>::rne(a)) | static_cast<uint32_t>(DtOps<DT>::rne(b)) << 16;
-        } else {  // integers below 256 are exact in bf16: the top half of the fp32 pattern
-            f.v[i] = (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
+        const uint32_t w = i < 2 ? lo8 : hi8;
+        uint32_t hh = 0, ll = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float q = static_cast<float>((w >> (8 * (2 * (i & 1) + e))) & 0xFFu);
+            const float v = __fmaf_rn(DtOps<DT>::to_f32(static_cast<uint16_t>(sw[i] >> (16 * e))), q,
+                                      DtOps<DT>::to_f32(static_cast<uint16_t>(bw[i] >> (16 * e))));
+            const uint16_t vh = DtOps<DT>::rne(v);
+            hh |= static_cast<uint32_t>(vh) << (16 * e);
+            if constexpr (DT == DT_BF16)
+                ll |= static_cast<uint32_t>(DtOps<DT>::rne(v - DtOps<DT>::to_f32(vh))) << (16 * e);
         }
+        fh.v[i] = hh;
+        fl.v[i] = ll;
     }
-    return f;
 }
 
 template <int DT, int BITS, int RB>
@@ -152,40 +159,23 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __rest
             hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
             lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
             hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
-            const Frag qf = codes_frag<DT>(lo, hi);
-            // this lane's 8 rows: scales and biases
+            // this lane's 8 rows: scales and biases, and the dequantized weights
             const int kl = static_cast<int>(k0 - kc0) + 8 * jq;
             const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + kl);
             const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + kl);
-            Frag bf;
-            bf.v[0] = bv.x; bf.v[1] = bv.y; bf.v[2] = bv.z; bf.v[3] = bv.w;
             const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+            const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+            Frag wh, wl;
+            dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int m = 16 * b + p;
                 uint4 xv = make_uint4(0u, 0u, 0u, 0u);
                 if (m < M) xv = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K + k0 + 8 * jq);
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-                Frag xf, ah, al;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xf.v[i] = xw[i];
-                    uint32_t hh = 0, ll = 0;
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float a = DtOps<DT>::to_f32(static_cast<uint16_t>(xw[i] >> (16 * e))) *
-                                        DtOps<DT>::to_f32(static_cast<uint16_t>(sw[i] >> (16 * e)));
-                        const uint16_t ahi = DtOps<DT>::rne(a);
-                        const uint16_t alo = DtOps<DT>::rne(a - DtOps<DT>::to_f32(ahi));
-                        hh |= static_cast<uint32_t>(ahi) << (16 * e);
-                        ll |= static_cast<uint32_t>(alo) << (16 * e);
-                    }
-                    ah.v[i] = hh;
-                    al.v[i] = ll;
-                }
-                acc[b] = mf::mfma<DT>(ah, qf, acc[b]);
-                acc[b] = mf::mfma<DT>(al, qf, acc[b]);
-                acc[b] = mf::mfma<DT>(xf, bf, acc[b]);
+                Frag xf;
+                xf.v[0] = xv.x; xf.v[1] = xv.y; xf.v[2] = xv.z; xf.v[3] = xv.w;
+                acc[b] = mf::mfma<DT>(xf, wh, acc[b]);
+                if constexpr (DT == DT_BF16) acc[b] = mf::mfma<DT>(xf, wl, acc[b]);
             }
         }
         __syncthreads();  // (the staged scales are overwritten next, or the buffer reused below)
