@@ -32,7 +32,7 @@ EXPORTS = (
     "qmm_select_kernel", "qmm_kernel_supported", "qmm_packed_words", "qmm_strerror", "qmm_kernel_name",
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
-    "qmm_small_m_batched", "qmm_small_m_nt",
+    "qmm_small_m_batched", "qmm_small_m_nt", "qmm_small_m_nt_ws", "qmm_small_m_nt_workspace_bytes",
 )
 
 
@@ -67,6 +67,8 @@ def _load():
         "qmm_split_plan": (i32, [i32, i32, i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "qmm_small_m_batched": (i32, [i32, i32, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "qmm_small_m_nt": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "qmm_small_m_nt_ws": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "qmm_small_m_nt_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -93,6 +95,8 @@ qmm_small_m_split_forced = _lib.qmm_small_m_split_forced
 qmm_split_plan = _lib.qmm_split_plan
 qmm_small_m_batched = _lib.qmm_small_m_batched
 qmm_small_m_nt = _lib.qmm_small_m_nt
+qmm_small_m_nt_ws = _lib.qmm_small_m_nt_ws
+qmm_small_m_nt_workspace_bytes = _lib.qmm_small_m_nt_workspace_bytes
 
 
 def strerror(status: int) -> str:
@@ -231,8 +235,17 @@ def small_m_batched(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, bia
     return out
 
 
+def nt_workspace_bytes(dtype, bits: int, group_size: int, M: int, N: int, K: int) -> int:
+    """Bytes of workspace :func:`small_m_nt` with ``split=True`` needs (0: it runs unsplit)."""
+    r = int(_lib.qmm_small_m_nt_workspace_bytes(_dt(dtype), bits, group_size, M, N, K))
+    if r < 0:
+        raise QmmError(r, "qmm_small_m_nt_workspace_bytes")
+    return r
+
+
 def small_m_nt(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
-               group_size: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+               group_size: int, out: torch.Tensor | None = None, stream=None, split: bool = False,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] = x [M, K] . dequant(W) for W stored [K, N] and quantized along N
     (wq [K, N*bits/32], scales / biases [K, N/gs]: :func:`quantize` of a [K, N] matrix)."""
     for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
@@ -245,9 +258,18 @@ def small_m_nt(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
         _dev(out, "out")
-    _check(qmm_small_m_nt(_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(),
-                          scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
-           "qmm_small_m_nt")
+    args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+            biases.data_ptr(), out.data_ptr())
+    if not split:
+        _check(qmm_small_m_nt(*args, _stream(stream)), "qmm_small_m_nt")
+        return out
+    # K split (workspace entry point): a workspace of the planned size unless given
+    need = nt_workspace_bytes(x.dtype, bits, group_size, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(qmm_small_m_nt_ws(*args, ws_ptr, ws_bytes, _stream(stream)), "qmm_small_m_nt_ws")
     return out
 
 

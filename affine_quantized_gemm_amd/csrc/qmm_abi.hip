@@ -160,6 +160,33 @@ int qmm_small_m_nt(int dt, int bits, int group_size, int64_t M, int64_t N, int64
     return hip_status(qmm::launch_nt(a));
 }
 
+int64_t qmm_small_m_nt_workspace_bytes(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || K < 0) return QMM_ERR_INVALID_ARG;
+    int st = check_format(dt, bits, group_size, K, N);
+    if (st != QMM_OK) return st;
+    if (M > 64 || K < 32 || K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    const qmm::NtPlan p = qmm::nt_plan(M, N, K);
+    return p.split > 1 ? static_cast<int64_t>(p.split) * M * N * 4 : 0;
+}
+
+int qmm_small_m_nt_ws(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                      const uint32_t* wq, const void* scales, const void* biases, void* y, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+    const int64_t need = qmm_small_m_nt_workspace_bytes(dt, bits, group_size, M, N, K);
+    if (need < 0) return static_cast<int>(need);
+    if (workspace_bytes < 0) return QMM_ERR_INVALID_ARG;
+    if (M == 0) return QMM_OK;
+    int st = check_ptrs({x, wq, scales, biases, y});
+    if (st != QMM_OK) return st;
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_INVALID_ARG;
+        if (!aligned16(workspace)) return QMM_ERR_MISALIGNED;
+    }
+    qmm::MatmulArgs a{dt, bits, group_size, M, N, K, x, wq, scales, biases, y, static_cast<hipStream_t>(stream)};
+    a.part = static_cast<float*>(workspace);
+    return hip_status(qmm::launch_nt_split(a));
+}
+
 int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, int* kernel_id, int* split) {
     if (M < 0 || kernel_id == nullptr || split == nullptr) return QMM_ERR_INVALID_ARG;
     int st = check_format(dt, bits, group_size, N, K);

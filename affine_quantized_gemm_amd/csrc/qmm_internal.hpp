@@ -40,6 +40,15 @@ enum { TILE_CFG_16 = 0, TILE_CFG_64 = 1 };
 hipError_t launch_mfma_tile(const MatmulArgs& a, int cfg);
 // non-transposed weights (W [K, N], quantized along N): y = x . dequant(W)
 hipError_t launch_nt(const MatmulArgs& a);
+// ... with K split across 128-column workgroups where the plan splits
+// (fp32 partials [split][M][N] in a.part); otherwise as launch_nt
+struct NtPlan {
+    bool wide;   // 128-column workgroups
+    int split;   // K slices (1: unsplit, no workspace)
+    int64_t ks;  // rows per slice (a multiple of 32)
+};
+NtPlan nt_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nt_split(const MatmulArgs& a);
 // M <= 16: every format where the k-blocks fit; M 17..64, on 16-row blocks
 // (vector form, 16 wavefronts): 4-bit LDS-ring grids on shapes with more
 // 16-column tiles than column slots, else any width where 16 rows take one

@@ -198,6 +198,154 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __rest
     }
 }
 
+// Wide form: one workgroup owns 128 columns (8 tiles of 16, 2 wavefronts
+// per tile taking the steps in turn) of one slice of K (blockIdx.y), so that
+// the 8 tiles' wavefronts share each 64-byte sector of 4-bit rows through the
+// CU's L1 instead of 8 CUs each fetching it.  With more than one slice the
+// workgroup leaves fp32 partial outputs part[slice][M][N], added in slice
+// order by a second kernel.
+constexpr int NTW_TILES = 8;
+constexpr int NTW_KW = NT_W / NTW_TILES;
+constexpr int NTW_KC = 1024;       // rows of scales and biases staged at a time
+constexpr int NTW_GMAX = 128 / 32;  // groups 128 columns span at most
+
+template <int DT, int BITS, int RB, bool PART>
+__global__ __launch_bounds__(64 * NT_W, 4) void nt_wide_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ part, int M, int64_t N,
+    int64_t K, int gs, int64_t ks) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint16_t* const s_lds = reinterpret_cast<uint16_t*>(lds);  // [NTW_GMAX][NTW_KC]
+    uint16_t* const b_lds = s_lds + NTW_GMAX * NTW_KC;
+    float* const red = reinterpret_cast<float*>(lds);  // (after the last step)
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tile = wave % NTW_TILES;
+    const int kw = wave / NTW_TILES;
+    const int64_t n0g = 128 * static_cast<int64_t>(blockIdx.x);
+    const int64_t n0 = n0g + 16 * tile;
+    const bool live = n0 < N;  // (uniform per wavefront: the last workgroup may hold 64 columns)
+    const int64_t G = N / gs;
+    const int64_t g0 = n0g / gs;
+    const int wcols = static_cast<int>(N - n0g < 128 ? N - n0g : 128);
+    const int gcount = (wcols + gs - 1) / gs;  // groups the workgroup's columns span
+    const int gi = 16 * tile / gs;
+    const int64_t row_words = N * BITS / 32;
+    const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * ks;
+    const int64_t kend = kbeg + ks < K ? kbeg + ks : K;
+
+    const int h = lane & 1;
+    const int kk = lane >> 1;
+    const int r = kk & 7;
+    const int p = lane & 15;
+    const int jq = lane >> 4;
+
+    float4_t acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[b] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int64_t kc0 = kbeg; kc0 < kend; kc0 += NTW_KC) {
+        const int kc = static_cast<int>(kend - kc0 < NTW_KC ? kend - kc0 : NTW_KC);
+        for (int t = threadIdx.x; t < gcount * kc; t += 64 * NT_W) {
+            const int gg = t / kc, k = t % kc;
+            s_lds[gg * NTW_KC + k] = scales[(kc0 + k) * G + g0 + gg];
+            b_lds[gg * NTW_KC + k] = biases[(kc0 + k) * G + g0 + gg];
+        }
+        __syncthreads();
+        if (live) {
+            for (int step = kw; step < kc / 32; step += NTW_KW) {
+                const int64_t k0 = kc0 + 32 * static_cast<int64_t>(step);
+                uint32_t lo, hi;
+                load_codes<BITS>(wq + (k0 + kk) * row_words, n0, h, lo, hi);
+                {
+                    const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
+                    if (r & 4) lo = phi;
+                    else hi = plo;
+                }
+                lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
+                hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
+                lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
+                hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+                const int kl = static_cast<int>(k0 - kc0) + 8 * jq;
+                const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + gi * NTW_KC + kl);
+                const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + gi * NTW_KC + kl);
+                const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+                const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+                Frag wh, wl;
+                dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    const int m = 16 * b + p;
+                    uint4 xv = make_uint4(0u, 0u, 0u, 0u);
+                    if (m < M) xv = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K + k0 + 8 * jq);
+                    Frag xf;
+                    xf.v[0] = xv.x; xf.v[1] = xv.y; xf.v[2] = xv.z; xf.v[3] = xv.w;
+                    acc[b] = mf::mfma<DT>(xf, wh, acc[b]);
+                    if constexpr (DT == DT_BF16) acc[b] = mf::mfma<DT>(xf, wl, acc[b]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // the 2 wavefronts of each tile: red[((w RB + b) 4 + q) 64 + lane], w = kw * 8 + tile
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[((wave * RB + b) * 4 + q) * 64 + lane] = acc[b][q];
+    __syncthreads();
+    for (int t = threadIdx.x; t < NTW_TILES * RB * 4 * 64; t += 64 * NT_W) {
+        const int ln = t & 63, q = (t >> 6) & 3, b = (t >> 8) % RB, tl = t / (256 * RB);
+        const int64_t tn0 = n0g + 16 * tl;
+        if (tn0 >= N) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NTW_KW; ++w) v += red[(((w * NTW_TILES + tl) * RB + b) * 4 + q) * 64 + ln];
+        const int m = 16 * b + 4 * (ln >> 4) + q;
+        const int pp = ln & 15;
+        const int64_t n = tn0 + 8 * (pp & 1) + (pp >> 1);
+        if (m < M) {
+            if constexpr (PART)
+                part[(static_cast<int64_t>(blockIdx.y) * M + m) * N + n] = v;
+            else
+                y[static_cast<int64_t>(m) * N + n] = DtOps<DT>::rne(v);
+        }
+    }
+}
+
+template <int DT, int BITS, int RB, bool PART>
+hipError_t launch_nt_wide_t(const MatmulArgs& a, int split, int64_t ks) {
+    const size_t lds_sb = 2 * NTW_GMAX * NTW_KC * sizeof(uint16_t);
+    const size_t lds_red = static_cast<size_t>(NT_W) * RB * 4 * 64 * sizeof(float);
+    const size_t lds = lds_sb > lds_red ? lds_sb : lds_red;
+    hipLaunchKernelGGL((nt_wide_kernel<DT, BITS, RB, PART>),
+                       dim3(static_cast<unsigned>((a.N + 127) / 128), static_cast<unsigned>(split)), dim3(64 * NT_W),
+                       lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
+                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
+                       static_cast<uint16_t*>(a.y), a.part, static_cast<int>(a.M), a.N, a.K, a.gs, ks);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if constexpr (PART) return launch_reduce_partials(DT, a.part, a.y, split, a.M * a.N, a.stream);
+    return hipSuccess;
+}
+
+template <int DT, int BITS, int RB>
+hipError_t launch_nt_wide_r(const MatmulArgs& a, int split, int64_t ks) {
+    return split > 1 ? launch_nt_wide_t<DT, BITS, RB, true>(a, split, ks)
+                     : launch_nt_wide_t<DT, BITS, RB, false>(a, split, ks);
+}
+
+template <int DT, int BITS>
+hipError_t launch_nt_wide_b(const MatmulArgs& a, int split, int64_t ks) {
+    switch ((a.M + 15) / 16) {
+        case 1: return launch_nt_wide_r<DT, BITS, 1>(a, split, ks);
+        case 2: return launch_nt_wide_r<DT, BITS, 2>(a, split, ks);
+        case 3: return launch_nt_wide_r<DT, BITS, 3>(a, split, ks);
+        case 4: return launch_nt_wide_r<DT, BITS, 4>(a, split, ks);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int DT, int BITS, int RB>
 hipError_t launch_nt_t(const MatmulArgs& a) {
     const size_t lds_sb = 2 * NT_KC * sizeof(uint16_t);
@@ -223,11 +371,43 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
 
 }  // namespace
 
+// K split of the workspace entry point: 128-column workgroups, slices enough
+// for about 256 workgroups (at most 16, at least 2 steps of 32 rows each);
+// wide N (>= 128 such workgroups) runs unsplit.
+NtPlan nt_plan(int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    NtPlan p{false, 1, K};
+    const int64_t groups = (N + 127) / 128;  // 128-column workgroups
+    if (groups >= 128) return NtPlan{true, 1, K};  // wide N: enough workgroups unsplit
+    int64_t split = 256 / groups;
+    if (split > 16) split = 16;
+    if (split > K / 64) split = K / 64;
+    if (split < 2) return p;
+    const int64_t ks = ((K + split - 1) / split + 31) / 32 * 32;  // rows per slice, whole 32-row steps
+    return NtPlan{true, static_cast<int>((K + ks - 1) / ks), ks};
+}
+
+namespace {
+bool nt_shape_ok(const MatmulArgs& a) {
+    return a.M >= 1 && a.M <= 64 && a.N >= 64 && a.N % 64 == 0 && a.gs >= 32 && a.N % a.gs == 0 && a.K >= 32 &&
+           a.K % 32 == 0;
+}
+}  // namespace
+
 hipError_t launch_nt(const MatmulArgs& a) {
-    // shapes the kernel assumes (validated by the caller)
-    if (a.M < 1 || a.M > 64 || a.N < 64 || a.N % 64 != 0 || a.N % a.gs != 0 || a.gs < 32 || a.K < 32 ||
-        a.K % 32 != 0)
-        return hipErrorInvalidValue;
+    // shapes the kernels assume (validated by the caller)
+    if (!nt_shape_ok(a)) return hipErrorInvalidValue;
+    if ((a.N + 127) / 128 >= 128) {  // wide N: the 128-column form, unsplit
+        switch (a.dt * 10 + a.bits) {
+            case 4: return launch_nt_wide_b<DT_F16, 4>(a, 1, a.K);
+            case 6: return launch_nt_wide_b<DT_F16, 6>(a, 1, a.K);
+            case 8: return launch_nt_wide_b<DT_F16, 8>(a, 1, a.K);
+            case 14: return launch_nt_wide_b<DT_BF16, 4>(a, 1, a.K);
+            case 16: return launch_nt_wide_b<DT_BF16, 6>(a, 1, a.K);
+            case 18: return launch_nt_wide_b<DT_BF16, 8>(a, 1, a.K);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.dt * 10 + a.bits) {
         case 4: return launch_nt_b<DT_F16, 4>(a);
         case 6: return launch_nt_b<DT_F16, 6>(a);
@@ -235,6 +415,22 @@ hipError_t launch_nt(const MatmulArgs& a) {
         case 14: return launch_nt_b<DT_BF16, 4>(a);
         case 16: return launch_nt_b<DT_BF16, 6>(a);
         case 18: return launch_nt_b<DT_BF16, 8>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_nt_split(const MatmulArgs& a) {
+    if (!nt_shape_ok(a)) return hipErrorInvalidValue;
+    const NtPlan p = nt_plan(a.M, a.N, a.K);
+    if (p.split < 2) return launch_nt(a);
+    if (a.part == nullptr) return hipErrorInvalidValue;
+    switch (a.dt * 10 + a.bits) {
+        case 4: return launch_nt_wide_b<DT_F16, 4>(a, p.split, p.ks);
+        case 6: return launch_nt_wide_b<DT_F16, 6>(a, p.split, p.ks);
+        case 8: return launch_nt_wide_b<DT_F16, 8>(a, p.split, p.ks);
+        case 14: return launch_nt_wide_b<DT_BF16, 4>(a, p.split, p.ks);
+        case 16: return launch_nt_wide_b<DT_BF16, 6>(a, p.split, p.ks);
+        case 18: return launch_nt_wide_b<DT_BF16, 8>(a, p.split, p.ks);
         default: return hipErrorInvalidValue;
     }
 }

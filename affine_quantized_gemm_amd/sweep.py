@@ -244,10 +244,21 @@ def sweep_nt(stack_mib):
                     Q.small_m_nt(x, wq, sc, bi, bits, gs, out=y)
 
             t = round(time_calls(run, len(stack)), 3)
+            need = Q.nt_workspace_bytes(tdt, bits, gs, M, N, K)
+            ws = torch.empty((max(need, 16),), dtype=torch.uint8, device="cuda")
+
+            def run_split():
+                for (wq, sc, bi) in stack:
+                    Q.small_m_nt(x, wq, sc, bi, bits, gs, out=y, split=True, workspace=ws)
+
+            ts = round(time_calls(run_split, len(stack)), 3)
             row = {"shape": name, "N": N, "K": K, "dt": dt, "bits": bits, "gs": gs, "M": M, "nt_us": t,
-                   "nt_gbs": round(B / (t * 1e-6) / 1e9, 1)}
+                   "nt_gbs": round(B / (t * 1e-6) / 1e9, 1), "nt_split_us": ts,
+                   "nt_split_gbs": round(B / (ts * 1e-6) / 1e9, 1), "workspace_bytes": need}
             rows.append(row)
-            print(f"nt {name:8s} M={M:3d}  {t:8.2f} us  ({row['nt_gbs']} GB/s)", flush=True)
+            print(f"nt {name:8s} M={M:3d}  {t:8.2f} us  ({row['nt_gbs']} GB/s)   with the K split {ts:8.2f} us "
+                  f"({row['nt_split_gbs']} GB/s)", flush=True)
+            del ws
         del stack
         torch.cuda.empty_cache()
     return rows

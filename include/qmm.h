@@ -153,6 +153,26 @@ int qmm_small_m_nt(int dt, int bits, int group_size, int64_t M, int64_t N, int64
                    const void* x, const uint32_t* wq, const void* scales,
                    const void* biases, void* y, void* stream);
 
+/*
+ * Non-transposed weights with K split across workgroups: as qmm_small_m_nt,
+ * with 128-column workgroups each taking one slice of K and leaving fp32
+ * partial outputs ([split][M][N]) in a caller-provided workspace; a second
+ * kernel adds them in slice order and rounds once (deterministic).  The
+ * slices are chosen to give about 256 workgroups (at most 16 slices).
+ * Where the plan does not split (wide N, short K) the workspace may be NULL
+ * and the call is exactly qmm_small_m_nt.
+ * qmm_small_m_nt_workspace_bytes: bytes of workspace the call needs (0: no
+ * split), or a negative status.  Pure host logic.
+ * qmm_small_m_nt_ws: workspace is caller-owned device memory of
+ * workspace_bytes >= that, 16-byte aligned, not aliasing the other arrays;
+ * too small or NULL when needed -> QMM_ERR_INVALID_ARG, misaligned ->
+ * QMM_ERR_MISALIGNED.  Two calls in flight need two workspaces.
+ */
+int64_t qmm_small_m_nt_workspace_bytes(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K);
+int qmm_small_m_nt_ws(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                      const void* x, const uint32_t* wq, const void* scales, const void* biases,
+                      void* y, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* As qmm_small_m with the variant forced (measurement and tests).
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
  * (QMM_KERNEL_MFMA_REG needs K <= 4096; for M = 17..64 it runs on 16-row

@@ -313,3 +313,28 @@ def test_nt_validation():
     assert nt(0, 4, 64, 4, 256, 64, A, None, A, A, A, None) == Q.QMM_ERR_INVALID_ARG
     assert nt(0, 4, 64, 4, 256, 64, A, A, A, MIS, A, None) == Q.QMM_ERR_MISALIGNED
     assert nt(1, 6, 32, 0, 256, 64, None, None, None, None, None, None) == Q.QMM_OK
+
+
+def test_nt_split_plan_and_validation():
+    """qmm_small_m_nt_ws: 128-column workgroups with K slices for about 256
+    workgroups (at most 16); unsplit where N gives 128 such workgroups or K
+    is short; errors before any HIP call."""
+    f16 = Q.QMM_F16
+    wb = Q.qmm_small_m_nt_workspace_bytes
+    assert wb(f16, 4, 64, 6, 4096, 4096) == 8 * 6 * 4096 * 4       # 32 workgroups x 8 slices
+    assert wb(f16, 4, 64, 6, 1024, 4096) == 16 * 6 * 1024 * 4      # capped at 16 slices
+    assert wb(f16, 4, 64, 4, 4096, 14336) == 8 * 4 * 4096 * 4
+    assert wb(f16, 4, 64, 64, 1024, 4160) == 15 * 64 * 1024 * 4    # slices of 288 rows, the last shorter
+    assert wb(f16, 4, 64, 6, 16384, 4096) == 0                     # 128 workgroups: unsplit
+    assert wb(f16, 4, 64, 6, 256, 96) == 0                         # one slice of K
+    assert wb(f16, 4, 64, -1, 256, 96) == Q.QMM_ERR_INVALID_ARG
+    assert wb(f16, 4, 64, 6, 96, 96) == Q.QMM_ERR_UNSUPPORTED
+    ws = Q.qmm_small_m_nt_ws
+    base = (f16, 4, 64, 6, 4096, 4096, A, A, A, A, A)
+    need = 8 * 6 * 4096 * 4
+    assert ws(*base, A, need - 4, None) == Q.QMM_ERR_INVALID_ARG
+    assert ws(*base, None, need, None) == Q.QMM_ERR_INVALID_ARG
+    assert ws(*base, MIS, need, None) == Q.QMM_ERR_MISALIGNED
+    assert ws(*base, A, -1, None) == Q.QMM_ERR_INVALID_ARG
+    assert ws(f16, 4, 64, 6, 4096, 4096, None, A, A, A, A, A, need, None) == Q.QMM_ERR_INVALID_ARG
+    assert ws(f16, 4, 64, 0, 4096, 4096, None, None, None, None, None, None, 0, None) == Q.QMM_OK

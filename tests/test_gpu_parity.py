@@ -418,6 +418,36 @@ def test_nt_shapes(Q, dt, bits, gs, M, N, K):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # deterministic
 
 
+@pytest.mark.parametrize("dt,bits,gs,M,N,K", [
+    ("f16", 4, 64, 6, 4096, 4096),      # 32 workgroups of 128 columns x 8 slices
+    ("bf16", 6, 128, 36, 384, 640),     # 3 workgroups x 10 slices of 64 rows
+    ("f16", 8, 32, 16, 64, 8192),       # one workgroup holding 64 columns, 16 slices
+    ("bf16", 4, 32, 64, 1024, 4160),    # 15 slices, the last one shorter
+    ("f16", 4, 64, 4, 16448, 256),      # 129 workgroups: unsplit, the last one 64 columns wide
+])
+def test_nt_split(Q, dt, bits, gs, M, N, K):
+    """Non-transposed weights with K split across 128-column workgroups (and
+    the unsplit 128-column form for wide N): every output against the
+    oracle, two calls bit-identical."""
+    print(f"nt split {dt} {bits}-bit gs{gs} M={M} N={N} K={K} "
+          f"workspace={Q.nt_workspace_bytes(DT[dt], bits, gs, M, N, K)}", flush=True)
+    w = synth.normal((K, N), 0.02, dt, 9900 + M, outlier_frac=0.01)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    x = synth.normal((M, K), 1.0, dt, 9901 + M)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    xc = x.cuda()
+    y = Q.small_m_nt(xc, wq, sc, bi, bits, gs, split=True)
+    torch.cuda.synchronize()
+    yo, T = O.qmm_nt(synth.to_oracle(x), owq, osc, obi, dt, bits, gs, N)
+    ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+    assert ok, worst
+    y2 = Q.small_m_nt(xc, wq, sc, bi, bits, gs, split=True)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    y3 = Q.small_m_nt(xc, wq, sc, bi, bits, gs)
+    ok3, worst3 = O.within_tolerance(O.to_f64(synth.to_oracle(y3), dt), yo, T)
+    assert ok3, worst3
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
