@@ -70,6 +70,44 @@ __device__ __forceinline__ void load_codes(const uint32_t* __restrict__ row, int
     }
 }
 
+// The same as two parts: the words holding the codes (loaded ahead), then
+// the widening to bytes.
+template <int BITS>
+__device__ __forceinline__ void load_words(const uint32_t* __restrict__ row, int64_t n0, int h, uint32_t& a,
+                                           uint32_t& b) {
+    if constexpr (BITS == 4) {
+        a = row[n0 / 8 + h];
+        b = 0u;
+    } else if constexpr (BITS == 8) {
+        a = row[n0 / 4 + 2 * h];
+        b = row[n0 / 4 + 2 * h + 1];
+    } else {
+        a = row[n0 / 16 * 3 + h];
+        b = row[n0 / 16 * 3 + h + 1];
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void widen_words(uint32_t a, uint32_t b, int h, uint32_t& lo, uint32_t& hi) {
+    if constexpr (BITS == 4) {
+        auto spread = [](uint32_t t) {
+            return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
+        };
+        lo = spread(a & 0xFFFFu);
+        hi = spread(a >> 16);
+    } else if constexpr (BITS == 8) {
+        lo = a;
+        hi = b;
+    } else {
+        const uint64_t u = (static_cast<uint64_t>(b) << 32 | a) >> (16 * h);
+        uint32_t c8[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) c8[c] = static_cast<uint32_t>(u >> (6 * c)) & 63u;
+        lo = c8[0] | c8[1] << 8 | c8[2] << 16 | c8[3] << 24;
+        hi = c8[4] | c8[5] << 8 | c8[6] << 16 | c8[7] << 24;
+    }
+}
+
 // one merge stage of the transpose on one word: lanes whose row bit is
 // clear keep their low part and take the partner's low part shifted up;
 // the others take the partner's high part shifted down and keep their own
@@ -203,10 +241,15 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __rest
 // the 8 tiles' wavefronts share each 64-byte sector of 4-bit rows through the
 // CU's L1 instead of 8 CUs each fetching it.  With more than one slice the
 // workgroup leaves fp32 partial outputs part[slice][M][N], added in slice
-// order by a second kernel.
+// order by a second kernel.  Per chunk of 512 rows a wavefront issues all 8
+// of its weight loads before computing, and the workgroup stages the
+// chunk's activation rows in LDS, so that a chunk waits about one memory
+// latency.
 constexpr int NTW_TILES = 8;
 constexpr int NTW_KW = NT_W / NTW_TILES;
-constexpr int NTW_KC = 1024;       // rows of scales and biases staged at a time
+constexpr int NTW_STEPS = 8;                       // 32-row steps of a wavefront per chunk
+constexpr int NTW_KC = 32 * NTW_KW * NTW_STEPS;    // rows per chunk (512)
+constexpr int NTW_XS = NTW_KC + 8;                 // activation row stride in LDS (16 bytes of padding)
 constexpr int NTW_GMAX = 128 / 32;  // groups 128 columns span at most
 
 template <int DT, int BITS, int RB, bool PART>
@@ -217,6 +260,7 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_wide_kernel(
     extern __shared__ __align__(16) uint8_t lds[];
     uint16_t* const s_lds = reinterpret_cast<uint16_t*>(lds);  // [NTW_GMAX][NTW_KC]
     uint16_t* const b_lds = s_lds + NTW_GMAX * NTW_KC;
+    uint16_t* const x_lds = b_lds + NTW_GMAX * NTW_KC;        // [M][NTW_XS]
     float* const red = reinterpret_cast<float*>(lds);  // (after the last step)
 
     const int lane = threadIdx.x & 63;
@@ -247,43 +291,61 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_wide_kernel(
 
     for (int64_t kc0 = kbeg; kc0 < kend; kc0 += NTW_KC) {
         const int kc = static_cast<int>(kend - kc0 < NTW_KC ? kend - kc0 : NTW_KC);
+        // this wavefront's weight loads of the chunk first (steps kw, kw + 2,
+        // ...), all in flight together; then the chunk's activation rows and
+        // scales and biases, staged in LDS by the whole workgroup
+        const int nst = live ? (kc / 32 - kw + NTW_KW - 1) / NTW_KW : 0;
+        uint32_t wa[NTW_STEPS], wb[NTW_STEPS];
+#pragma unroll
+        for (int i = 0; i < NTW_STEPS; ++i) {
+            wa[i] = wb[i] = 0u;
+            if (i < nst)
+                load_words<BITS>(wq + (kc0 + 32 * static_cast<int64_t>(kw + i * NTW_KW) + kk) * row_words, n0, h,
+                                 wa[i], wb[i]);
+        }
+        const int cpr = kc / 8;  // 16-byte pieces per activation row of the chunk
+        for (int t = threadIdx.x; t < M * cpr; t += 64 * NT_W) {
+            const int m = t / cpr, c8 = t % cpr;
+            *reinterpret_cast<uint4*>(x_lds + m * NTW_XS + 8 * c8) =
+                *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K + kc0 + 8 * c8);
+        }
         for (int t = threadIdx.x; t < gcount * kc; t += 64 * NT_W) {
             const int gg = t / kc, k = t % kc;
             s_lds[gg * NTW_KC + k] = scales[(kc0 + k) * G + g0 + gg];
             b_lds[gg * NTW_KC + k] = biases[(kc0 + k) * G + g0 + gg];
         }
         __syncthreads();
-        if (live) {
-            for (int step = kw; step < kc / 32; step += NTW_KW) {
-                const int64_t k0 = kc0 + 32 * static_cast<int64_t>(step);
-                uint32_t lo, hi;
-                load_codes<BITS>(wq + (k0 + kk) * row_words, n0, h, lo, hi);
-                {
-                    const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
-                    if (r & 4) lo = phi;
-                    else hi = plo;
-                }
-                lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
-                hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
-                lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
-                hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
-                const int kl = static_cast<int>(k0 - kc0) + 8 * jq;
-                const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + gi * NTW_KC + kl);
-                const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + gi * NTW_KC + kl);
-                const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-                const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-                Frag wh, wl;
-                dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
 #pragma unroll
-                for (int b = 0; b < RB; ++b) {
-                    const int m = 16 * b + p;
-                    uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-                    if (m < M) xv = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K + k0 + 8 * jq);
-                    Frag xf;
-                    xf.v[0] = xv.x; xf.v[1] = xv.y; xf.v[2] = xv.z; xf.v[3] = xv.w;
-                    acc[b] = mf::mfma<DT>(xf, wh, acc[b]);
-                    if constexpr (DT == DT_BF16) acc[b] = mf::mfma<DT>(xf, wl, acc[b]);
-                }
+        for (int i = 0; i < NTW_STEPS; ++i) {
+            if (i >= nst) break;
+            const int kl0 = 32 * (kw + i * NTW_KW);  // step's first row in the chunk
+            uint32_t lo, hi;
+            widen_words<BITS>(wa[i], wb[i], h, lo, hi);
+            {
+                const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
+                if (r & 4) lo = phi;
+                else hi = plo;
+            }
+            lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
+            hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
+            lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
+            hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+            const int kl = kl0 + 8 * jq;
+            const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + gi * NTW_KC + kl);
+            const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + gi * NTW_KC + kl);
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+            const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+            Frag wh, wl;
+            dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int m = 16 * b + p;
+                uint4 xv = make_uint4(0u, 0u, 0u, 0u);
+                if (m < M) xv = *reinterpret_cast<const uint4*>(x_lds + m * NTW_XS + kl);
+                Frag xf;
+                xf.v[0] = xv.x; xf.v[1] = xv.y; xf.v[2] = xv.z; xf.v[3] = xv.w;
+                acc[b] = mf::mfma<DT>(xf, wh, acc[b]);
+                if constexpr (DT == DT_BF16) acc[b] = mf::mfma<DT>(xf, wl, acc[b]);
             }
         }
         __syncthreads();
@@ -316,9 +378,16 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_wide_kernel(
 
 template <int DT, int BITS, int RB, bool PART>
 hipError_t launch_nt_wide_t(const MatmulArgs& a, int split, int64_t ks) {
-    const size_t lds_sb = 2 * NTW_GMAX * NTW_KC * sizeof(uint16_t);
+    const size_t lds_sb = 2 * NTW_GMAX * NTW_KC * sizeof(uint16_t) + 16 * RB * NTW_XS * sizeof(uint16_t);
     const size_t lds_red = static_cast<size_t>(NT_W) * RB * 4 * 64 * sizeof(float);
     const size_t lds = lds_sb > lds_red ? lds_sb : lds_red;
+    if (lds > 65536) {
+        // above the default dynamic-LDS limit: raise it once per kernel
+        static const hipError_t attr =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&nt_wide_kernel<DT, BITS, RB, PART>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (attr != hipSuccess) return attr;
+    }
     hipLaunchKernelGGL((nt_wide_kernel<DT, BITS, RB, PART>),
                        dim3(static_cast<unsigned>((a.N + 127) / 128), static_cast<unsigned>(split)), dim3(64 * NT_W),
                        lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
