@@ -211,12 +211,12 @@ int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, i
  * qmm_small_m_split_forced: the same with the variant and split forced
  * (measurement and tests).  split >= 1.  split > 1 with a TILE variant is
  * reduced to the largest count that gives every split part of K; with
- * QMM_KERNEL_MFMA_REG (4-bit, M <= 16) K must be exactly `split` slices of
- * a depth that variant covers split-free (K/split in {2048, 4096} with
- * group sizes whose scale rows split evenly), with more 16-column tiles
- * than 256/split, else QMM_ERR_UNSUPPORTED -- that is how it runs K it
- * cannot take whole.  The workspace must hold that many [M][N] fp32
- * outputs.
+ * QMM_KERNEL_MFMA_REG (4-bit; above 16 rows on 16-row blocks) K must be
+ * exactly `split` slices of a depth that variant covers split-free
+ * (K/split in {2048, 4096} with group sizes whose scale rows split evenly),
+ * with more 16-column tiles than 256 / (split x row blocks), else
+ * QMM_ERR_UNSUPPORTED -- that is how it runs K it cannot take whole.  The
+ * workspace must hold that many [M][N] fp32 outputs.
  *
  * qmm_split_plan: the variant and split qmm_small_m_ws uses.  Pure host
  * logic.
