@@ -221,11 +221,11 @@ NT_SHAPES = ("verify", "kv", "gateup", "down")
 NT_MS = (1, 6, 16, 64)
 
 
-def sweep_nt(stack_mib):
+def sweep_nt(stack_mib, shapes=NT_SHAPES):
     """qmm_small_m_nt (W stored [K, N], quantized along N) next to the
     transposed call on the same shape, over stacks larger than the caches."""
     rows = []
-    for name in NT_SHAPES:
+    for name in shapes:
         N, K, dt, bits, gs = SHAPES[name]
         tdt = synth.TORCH_DT[dt]
         B = weight_bytes(N, K, bits, gs)
@@ -274,6 +274,7 @@ def main():
     p.add_argument("--layer", action="store_true", help="also sum one decoder layer's projections per M")
     p.add_argument("--batched", action="store_true", help="also time the batched entry point")
     p.add_argument("--nt", action="store_true", help="also time non-transposed weights")
+    p.add_argument("--nt-shapes", default=",".join(NT_SHAPES), help="shapes for --nt")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
     shapes = [s for s in a.shapes.split(",") if s]
@@ -294,7 +295,7 @@ def main():
         out = dict(out) if isinstance(out, dict) else {"rows": rows}
         out["batched"] = brows
     if a.nt:
-        nrows = sweep_nt(a.stack_mib)
+        nrows = sweep_nt(a.stack_mib, [s for s in a.nt_shapes.split(",") if s])
         out = dict(out) if isinstance(out, dict) else {"rows": rows}
         out["nt"] = nrows
     if a.json:
