@@ -14,9 +14,10 @@
 //     of rows k0 + 8 (l / 16) .. + 8 of one column: the MFMA B operand.  The
 //     column a lane holds is c(p) = 8 (p % 2) + p / 2 for p = l % 16, a fixed
 //     relabeling undone at the store;
-//   * the lane dequantizes them, w = s q + b in fp32 (the scale and bias of
-//     each of its 8 rows), to the B operand hi = RNE_dt(w) -- the
-//     dequantizer's value -- and for bf16 also lo = RNE_dt(w - hi): with
+//   * the lane dequantizes them, w = s q + b (the scale and bias of each of
+//     its 8 rows): fp16 with packed fp16 arithmetic, rounded once; bf16 in
+//     fp32 to hi = RNE_bf16(w), the dequantizer's value, and
+//     lo = RNE_bf16(w - hi): with
 //     bf16's 8-bit significand one rounding of w and one of y could together
 //     exceed the accepted error, hi + lo carries w to about u^2;
 //   * partial 16 x 16 tiles of the wavefronts are added through LDS and
@@ -124,6 +125,27 @@ __device__ __forceinline__ uint32_t merge(uint32_t v, bool upper) {
 template <int DT>
 __device__ __forceinline__ void dequant_frags(uint32_t lo8, uint32_t hi8, const uint32_t (&sw)[4],
                                               const uint32_t (&bw)[4], Frag& fh, Frag& fl) {
+    if constexpr (DT == DT_F16) {
+        // packed fp16: two codes at a time become 1024 + q (a byte permute
+        // under the exponent byte 0x64), minus 1024 gives q exactly, and one
+        // fused multiply-add with the (already packed) scale and bias pair
+        // rounds s q + b once to fp16 -- within one fp16 rounding of w, as
+        // the fp32 route is
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        const half2_t off = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = i < 2 ? lo8 : hi8;
+            const uint32_t b0 = 2u * static_cast<uint32_t>(i & 1);
+            const uint32_t sel = b0 | (4u << 8) | ((b0 + 1u) << 16) | (4u << 24);
+            const half2_t q = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, w, sel)) - off;
+            const half2_t v = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, sw[i]), q,
+                                                        __builtin_bit_cast(half2_t, bw[i]));
+            fh.v[i] = __builtin_bit_cast(uint32_t, v);
+            fl.v[i] = 0u;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w = i < 2 ? lo8 : hi8;
