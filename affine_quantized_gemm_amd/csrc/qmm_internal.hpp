@@ -1,6 +1,7 @@
 // Launchers shared between the libqmm translation units (host side).
 #pragma once
 
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +32,19 @@ struct MatmulArgs {
     // dense size of one entry's array.
     int64_t batch = 1;
 };
+
+// Raise a kernel's dynamic-LDS limit to the CU's 160 KiB on the current
+// device, once per device (the attribute is a per-device setting; `done`
+// holds one bit per device id below 64, beyond that the call is repeated).
+inline hipError_t raise_lds_limit(const void* kernel, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 hipError_t launch_valu(const MatmulArgs& a);
 hipError_t launch_mfma_reg(const MatmulArgs& a);

@@ -279,10 +279,10 @@ hipError_t launch_pass_sv(const MatmulArgs& a) {
     const int64_t gx = ntiles < slots ? ntiles : slots;
     const size_t lds = static_cast<size_t>(PF::LDS_BYTES);
     if (lds > 65536) {
-        static const hipError_t attr =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_pass_kernel<DT, BITS, GS, SV>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (attr != hipSuccess) return attr;
+        static std::atomic<uint64_t> raised{0};
+        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mfma_pass_kernel<DT, BITS, GS, SV>), raised);
+            e != hipSuccess)
+            return e;
     }
     hipLaunchKernelGGL((mfma_pass_kernel<DT, BITS, GS, SV>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
                        dim3(64 * PW), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,

@@ -875,11 +875,13 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const size_t lds = reg_lds_bytes<DT, BITS, GS, W, KPW, VEC, MULTI, MH>(ROWS ? 16 : a.M, kr);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     if (lds > 65536) {
-        // above the default dynamic-LDS limit: raise it once per kernel
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (attr != hipSuccess) return attr;
+        // above the default dynamic-LDS limit: raise it once per kernel and device
+        static std::atomic<uint64_t> raised{0};
+        if (hipError_t e = raise_lds_limit(
+                reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
+                raised);
+            e != hipSuccess)
+            return e;
     }
     hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(SPLIT ? S : nb),

@@ -436,10 +436,11 @@ hipError_t launch_tile_cfg(const MatmulArgs& a) {
     const int64_t slots = 256 / S > 1 ? 256 / S : 1;
     const int64_t gx = ntiles < slots ? ntiles : slots;
     const size_t lds = static_cast<size_t>(TF::lds_bytes(rb));
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
+    static std::atomic<uint64_t> raised{0};
+    if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>),
+                                       raised);
+        e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((mfma_tile_kernel<DT, BITS, GS, CW, NT, KW, D>),
                        dim3(static_cast<unsigned>(gx), static_cast<unsigned>(S)), dim3(64 * TF::WAVES), lds,
                        a.stream, static_cast<const uint16_t*>(a.x), a.wq, static_cast<const uint16_t*>(a.scales),

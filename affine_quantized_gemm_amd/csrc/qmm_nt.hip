@@ -404,11 +404,11 @@ hipError_t launch_nt_wide_t(const MatmulArgs& a, int split, int64_t ks) {
     const size_t lds_red = static_cast<size_t>(NT_W) * RB * 4 * 64 * sizeof(float);
     const size_t lds = lds_sb > lds_red ? lds_sb : lds_red;
     if (lds > 65536) {
-        // above the default dynamic-LDS limit: raise it once per kernel
-        static const hipError_t attr =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&nt_wide_kernel<DT, BITS, RB, PART>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (attr != hipSuccess) return attr;
+        // above the default dynamic-LDS limit: raise it once per kernel and device
+        static std::atomic<uint64_t> raised{0};
+        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&nt_wide_kernel<DT, BITS, RB, PART>), raised);
+            e != hipSuccess)
+            return e;
     }
     hipLaunchKernelGGL((nt_wide_kernel<DT, BITS, RB, PART>),
                        dim3(static_cast<unsigned>((a.N + 127) / 128), static_cast<unsigned>(split)), dim3(64 * NT_W),
