@@ -448,6 +448,46 @@ def test_nt_split(Q, dt, bits, gs, M, N, K):
     assert ok3, worst3
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_nt_smallest_shapes(Q, dt, bits):
+    """The smallest non-transposed problems: K = 32 (one step), N = 64 (one
+    workgroup of the split form holding half its columns), M = 1 and 17;
+    split-free and with the K split, every output."""
+    gs = 32
+    for M, N, K in ((1, 64, 32), (17, 64, 32), (1, 64, 128), (17, 192, 64)):
+        print(f"nt smallest {dt} {bits}-bit M={M} N={N} K={K}", flush=True)
+        w = synth.normal((K, N), 0.02, dt, 9950 + bits + K)
+        owq, osc, obi = oracle_quant(w, dt, bits, gs)
+        x = synth.normal((M, K), 1.0, dt, 9951 + M)
+        wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+        yo, T = O.qmm_nt(synth.to_oracle(x), owq, osc, obi, dt, bits, gs, N)
+        for split in (False, True):
+            y = Q.small_m_nt(x.cuda(), wq, sc, bi, bits, gs, split=split)
+            torch.cuda.synchronize()
+            ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+            assert ok, (M, N, K, split, worst)
+
+
+def test_batched_and_nt_empty_problems(Q):
+    """Empty batched and non-transposed problems launch nothing and return
+    empty outputs of the right shapes."""
+    x = torch.zeros((0, 4, 256), dtype=torch.float16, device="cuda")
+    wq = torch.zeros((0, 64, 32), dtype=torch.int32, device="cuda")
+    sb = torch.zeros((0, 64, 4), dtype=torch.float16, device="cuda")
+    assert Q.small_m_batched(x, wq, sb, sb, 4, 64).shape == (0, 4, 64)
+    w = synth.normal((3, 64, 256), 0.02, "f16", 1).cuda()
+    qs = [Q.quantize(w[b], 4, 64) for b in range(3)]
+    wq3, sc3, bi3 = (torch.stack([q[i] for q in qs]) for i in range(3))
+    x0 = torch.zeros((3, 0, 256), dtype=torch.float16, device="cuda")
+    assert Q.small_m_batched(x0, wq3, sc3, bi3, 4, 64).shape == (3, 0, 64)
+    wkn = synth.normal((256, 128), 0.02, "f16", 2).cuda()
+    wqn, scn, bin_ = Q.quantize(wkn, 4, 64)
+    xn = torch.zeros((0, 256), dtype=torch.float16, device="cuda")
+    assert Q.small_m_nt(xn, wqn, scn, bin_, 4, 64).shape == (0, 128)
+    assert Q.small_m_nt(xn, wqn, scn, bin_, 4, 64, split=True).shape == (0, 128)
+
+
 @pytest.mark.parametrize("dt,gs,K,splits", [("f16", 64, 14336, (7,)), ("bf16", 32, 8192, (2, 4)),
                                              ("f16", 128, 8192, (2,))])
 def test_reg_split_k(Q, dt, gs, K, splits):
