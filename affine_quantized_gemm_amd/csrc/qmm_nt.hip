@@ -8,9 +8,10 @@
 // contiguous.  One workgroup owns 16 output columns (inside one group, since
 // gs >= 32) for all of K; its 16 wavefronts take 32-row steps in turn:
 //   * a lane loads the 8 codes of row k0 + l/2, columns 8 (l % 2) .. + 8
-//     (4 / 6 / 8 bytes), and widens them to bytes;
-//   * an 8 x 8 byte transpose among the 8 lanes of equal (l / 16, l % 2)
-//     (three swizzle-and-merge stages, no LDS) leaves lane l with the codes
+//     (4 / 6 / 8 bytes), and widens 6/8-bit codes to bytes;
+//   * an 8 x 8 transpose among the 8 lanes of equal (l / 16, l % 2) (three
+//     swizzle-and-merge stages, no LDS; on nibbles in one word for 4-bit
+//     codes, on bytes in two words otherwise) leaves lane l with the codes
 //     of rows k0 + 8 (l / 16) .. + 8 of one column: the MFMA B operand.  The
 //     column a lane holds is c(p) = 8 (p % 2) + p / 2 for p = l % 16, a fixed
 //     relabeling undone at the store;
@@ -49,13 +50,9 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 template <int BITS>
 __device__ __forceinline__ void load_codes(const uint32_t* __restrict__ row, int64_t n0, int h, uint32_t& lo,
                                            uint32_t& hi) {
-    if constexpr (BITS == 4) {
-        const uint32_t w = row[n0 / 8 + h];
-        auto spread = [](uint32_t t) {  // 4 nibbles -> 4 bytes
-            return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
-        };
-        lo = spread(w & 0xFFFFu);
-        hi = spread(w >> 16);
+    if constexpr (BITS == 4) {  // (kept as nibbles: transposed as such)
+        lo = row[n0 / 8 + h];
+        hi = 0u;
     } else if constexpr (BITS == 8) {
         lo = row[n0 / 4 + 2 * h];
         hi = row[n0 / 4 + 2 * h + 1];
@@ -90,12 +87,9 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ row, int
 
 template <int BITS>
 __device__ __forceinline__ void widen_words(uint32_t a, uint32_t b, int h, uint32_t& lo, uint32_t& hi) {
-    if constexpr (BITS == 4) {
-        auto spread = [](uint32_t t) {
-            return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
-        };
-        lo = spread(a & 0xFFFFu);
-        hi = spread(a >> 16);
+    if constexpr (BITS == 4) {  // (kept as nibbles: transposed as such)
+        lo = a;
+        hi = 0u;
     } else if constexpr (BITS == 8) {
         lo = a;
         hi = b;
@@ -118,13 +112,59 @@ __device__ __forceinline__ uint32_t merge(uint32_t v, bool upper) {
     return upper ? ((p >> SHIFT) & MASK) | (v & ~MASK) : (v & MASK) | ((p & MASK) << SHIFT);
 }
 
+// The 8 x 8 transpose of a lane group's codes: afterwards lane r holds rows
+// 0..7 of column r.  Bytes (6/8-bit, widened) in two words, lo = columns /
+// rows 0..3 and hi = 4..7; 4-bit codes as nibbles in one word, row i at
+// bits 4 i (three stages on one word instead of widening first).
+template <int BITS>
+__device__ __forceinline__ void transpose_codes(uint32_t& lo, uint32_t& hi, int r) {
+    if constexpr (BITS == 4) {
+        lo = merge<8, 0x0000FFFFu, 16>(lo, (r & 4) != 0);
+        lo = merge<4, 0x00FF00FFu, 8>(lo, (r & 2) != 0);
+        lo = merge<2, 0x0F0F0F0Fu, 4>(lo, (r & 1) != 0);
+    } else {
+        // rows r, r ^ 4 (lanes 8 apart): swap the 4-column halves
+        const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
+        if (r & 4) lo = phi;
+        else hi = plo;
+        lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
+        hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
+        lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
+        hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+    }
+}
+
 // 8 codes (bytes, rows e = 0..7) -> the dequantized weights w = s q + b in
 // fp32 (s, b: 8 packed dt values each), as MFMA operands: hi = RNE_dt(w)
 // (the dequantizer's value) and, for bf16, lo = RNE_dt(w - hi), so that
 // hi + lo carries w to about u^2
-template <int DT>
+template <int DT, int BITS>
 __device__ __forceinline__ void dequant_frags(uint32_t lo8, uint32_t hi8, const uint32_t (&sw)[4],
                                               const uint32_t (&bw)[4], Frag& fh, Frag& fl) {
+    if constexpr (BITS == 4 && DT == DT_F16) {
+        // nibbles: 1024 + q for rows 2i, 2i + 1 from bits 8 i .. 8 i + 7
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        const half2_t off = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a = lo8 >> (8 * i);
+            const uint32_t d = 0x64006400u | (a & 0xFu) | ((a << 12) & 0xF0000u);
+            const half2_t q = __builtin_bit_cast(half2_t, d) - off;
+            const half2_t v = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, sw[i]), q,
+                                                        __builtin_bit_cast(half2_t, bw[i]));
+            fh.v[i] = __builtin_bit_cast(uint32_t, v);
+            fl.v[i] = 0u;
+        }
+        return;
+    }
+    if constexpr (BITS == 4) {  // bf16: nibbles to bytes, then as below
+        auto spread = [](uint32_t t) {
+            return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
+        };
+        const uint32_t w = lo8;
+        lo8 = spread(w & 0xFFFFu);
+        hi8 = spread(w >> 16);
+    }
     if constexpr (DT == DT_F16) {
         // packed fp16: two codes at a time become 1024 + q (a byte permute
         // under the exponent byte 0x64), minus 1024 gives q exactly, and one
@@ -209,16 +249,7 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __rest
             const int64_t k0 = kc0 + 32 * static_cast<int64_t>(step);
             uint32_t lo, hi;
             load_codes<BITS>(wq + (k0 + kk) * row_words, n0, h, lo, hi);
-            // rows r, r ^ 4 (lanes 8 apart): swap the 4-column halves
-            {
-                const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
-                if (r & 4) lo = phi;
-                else hi = plo;
-            }
-            lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
-            hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
-            lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
-            hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+            transpose_codes<BITS>(lo, hi, r);
             // this lane's 8 rows: scales and biases, and the dequantized weights
             const int kl = static_cast<int>(k0 - kc0) + 8 * jq;
             const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + kl);
@@ -226,7 +257,7 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_kernel(const uint16_t* __rest
             const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
             const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
             Frag wh, wl;
-            dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
+            dequant_frags<DT, BITS>(lo, hi, sw, bw, wh, wl);
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int m = 16 * b + p;
@@ -343,22 +374,14 @@ __global__ __launch_bounds__(64 * NT_W, 4) void nt_wide_kernel(
             const int kl0 = 32 * (kw + i * NTW_KW);  // step's first row in the chunk
             uint32_t lo, hi;
             widen_words<BITS>(wa[i], wb[i], h, lo, hi);
-            {
-                const uint32_t plo = xor_lane<8>(lo), phi = xor_lane<8>(hi);
-                if (r & 4) lo = phi;
-                else hi = plo;
-            }
-            lo = merge<4, 0x0000FFFFu, 16>(lo, (r & 2) != 0);
-            hi = merge<4, 0x0000FFFFu, 16>(hi, (r & 2) != 0);
-            lo = merge<2, 0x00FF00FFu, 8>(lo, (r & 1) != 0);
-            hi = merge<2, 0x00FF00FFu, 8>(hi, (r & 1) != 0);
+            transpose_codes<BITS>(lo, hi, r);
             const int kl = kl0 + 8 * jq;
             const uint4 sv = *reinterpret_cast<const uint4*>(s_lds + gi * NTW_KC + kl);
             const uint4 bv = *reinterpret_cast<const uint4*>(b_lds + gi * NTW_KC + kl);
             const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
             const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
             Frag wh, wl;
-            dequant_frags<DT>(lo, hi, sw, bw, wh, wl);
+            dequant_frags<DT, BITS>(lo, hi, sw, bw, wh, wl);
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int m = 16 * b + p;
