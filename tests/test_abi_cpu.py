@@ -338,3 +338,36 @@ def test_nt_split_plan_and_validation():
     assert ws(*base, A, -1, None) == Q.QMM_ERR_INVALID_ARG
     assert ws(f16, 4, 64, 6, 4096, 4096, None, A, A, A, A, A, need, None) == Q.QMM_ERR_INVALID_ARG
     assert ws(f16, 4, 64, 0, 4096, 4096, None, None, None, None, None, None, 0, None) == Q.QMM_OK
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """include/qmm.h is plain C (no torch, no C++): a C99 program compiles
+    against it with warnings as errors, links libqmm.so and gets the same
+    answers from the host-only entry points as the binding."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_qmm.c"
+    src.write_text(r'''
+#include "qmm.h"
+#include <stdio.h>
+int main(void) {
+    int k = -1, s = -1;
+    if (qmm_packed_words(4, 4096) != 512 || qmm_packed_words(6, 4096) != 768) return 1;
+    if (qmm_select_kernel(QMM_F16, 4, 64, 6, 4096, 4096) != QMM_KERNEL_MFMA_REG) return 2;
+    if (qmm_small_m(QMM_F16, 5, 64, 4, 64, 256, 0, 0, 0, 0, 0, 0) != QMM_ERR_UNSUPPORTED) return 3;
+    if (qmm_split_plan(QMM_F16, 4, 64, 8, 4096, 14336, &k, &s) != QMM_OK || k != QMM_KERNEL_MFMA_REG || s != 7) return 4;
+    if (qmm_small_m_nt_workspace_bytes(QMM_F16, 4, 64, 6, 4096, 4096) != 8LL * 6 * 4096 * 4) return 5;
+    if (qmm_small_m_batched(QMM_F16, 4, 64, 0, 4, 64, 256, 0, 0, 0, 0, 0, 0) != QMM_OK) return 6;
+    printf("%s\n", qmm_kernel_name(QMM_KERNEL_MFMA_REG));
+    return 0;
+}
+''')
+    exe = tmp_path / "use_qmm"
+    libdir = os.path.dirname(Q.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", libdir, "-lqmm", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip() == Q.kernel_name(Q.KERNEL_MFMA_REG)
