@@ -72,7 +72,13 @@ def parse():
     p.add_argument("--stack-mib", type=int, default=576, help="total weight bytes of the cycled stack")
     p.add_argument("--kernel", type=int, default=None, help="force a kernel variant")
     p.add_argument("--workspace", action="store_true",
-                   help="call qmm_small_m_ws (K split where its plan says so) instead of qmm_small_m")
+                   help="call qmm_small_m_ws (K split where its plan says so) instead of qmm_small_m "
+                        "(with --entry nt: qmm_small_m_nt_ws)")
+    p.add_argument("--entry", default="small_m", choices=("small_m", "batched", "nt"),
+                   help="small_m: y = x W^T per matrix; batched: qmm_small_m_batched over --batch entries, "
+                        "each with its own weights and activations; nt: weights stored [K, N] "
+                        "(qmm_small_m_nt)")
+    p.add_argument("--batch", type=int, default=8, help="entries per batched call (--entry batched)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extras", action="store_true",
@@ -91,6 +97,7 @@ KERNEL_SOURCES = {
     "mfma_splitfree_pass": ["qmm_mfma_pass.hip", "qmm_mfma_frag.hpp"],
     "mfma_splitfree_tile16": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
     "mfma_splitfree_tile64": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
+    "nt": ["qmm_nt.hip", "qmm_mfma_frag.hpp"],
 }
 COMMON_SOURCES = ["qmm_device.hpp", "qmm_internal.hpp"]
 
@@ -195,7 +202,7 @@ def traffic_from(fetch_dir, write_dir):
 
 # ---------------------------------------------------------------- oracle leg
 
-def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
+def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s, entry="small_m"):
     """The oracle, untuned, on one matrix of the workload (host cores).  For
     the LM head only a slice of the output columns is computed, scaled to a
     per-call figure (columns are independent)."""
@@ -208,20 +215,28 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     Ns = min(N, 16384)
-    w = synth.to_oracle(synth.normal((Ns, K), 0.02, dt, 9000))
+    if entry == "nt":  # weights [K, N] quantized along N: the whole matrix
+        Ns = N
+        w = synth.to_oracle(synth.normal((K, N), 0.02, dt, 9000))
+    else:
+        w = synth.to_oracle(synth.normal((Ns, K), 0.02, dt, 9000))
     wq, sc, bi = O.quantize(w, dt, bits, gs)
     xs = {M: synth.to_oracle(synth.normal((M, K), 1.0, dt, 9100 + M)) for M in Ms}
     calls = 0
     t0 = time.perf_counter()
     while True:
         for M in Ms:
-            O.qmm(xs[M], wq, sc, bi, dt, bits, gs)
+            if entry == "nt":
+                O.qmm_nt(xs[M], wq, sc, bi, dt, bits, gs, N)
+            else:  # (a batched call is this per entry)
+                O.qmm(xs[M], wq, sc, bi, dt, bits, gs)
             calls += 1
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
     per_call = el / calls * (N / Ns)
-    sample = (f"{calls} oracle calls (M in {list(Ms)}) on one {Ns}x{K} matrix"
+    sample = (f"{calls} oracle calls (M in {list(Ms)}) on one {Ns}x{K} matrix" + (" stored [K, N]" if entry == "nt" else "")
+              + (" (one entry of a batched call; per-entry figures)" if entry == "batched" else "")
               + (f" ({Ns} of the {N} output columns, time scaled by {N / Ns:.2f})" if Ns < N else "")
               + f", {el:.1f} s; {per_call * 1e6:.0f} us per full call")
     return {"value": round(weight_bytes(N, K, bits, gs) / per_call / 1e9, 4), "unit": "GB/s",
@@ -320,7 +335,10 @@ def main():
 
     dt, bits, gs, Ms, N, K = WORKLOADS[args.workload]
     tdt = synth.TORCH_DT[dt]
-    B = weight_bytes(N, K, bits, gs)
+    NB = args.batch if args.entry == "batched" else 1  # entries per call
+    if NB < 1:
+        raise SystemExit("--batch must be at least 1")
+    B = NB * weight_bytes(N, K, bits, gs)  # weight bytes of one call
     S = max(1, -(-(args.stack_mib << 20) // B))
     if args.workload == "tiny":
         S = 1
@@ -330,11 +348,23 @@ def main():
     # ---- synthetic weights, quantized on the GPU; raw weights freed right away
     stack = []
     for i in range(S):
-        w = synth.normal((N, K), 0.02, dt, synth.seed_for(2, 0, i), device=dev)
-        stack.append(Q.quantize(w, bits, gs))
-        del w
-    xs = {M: synth.normal((M, K), 1.0, dt, synth.seed_for(2, 1, M), device=dev) for M in Ms}
-    ys = {M: torch.empty((M, N), dtype=tdt, device=dev) for M in Ms}
+        if args.entry == "batched":  # one weight set per entry
+            ents = []
+            for b in range(NB):
+                w = synth.normal((N, K), 0.02, dt, synth.seed_for(2, 0, NB * i + b), device=dev)
+                ents.append(Q.quantize(w, bits, gs))
+                del w
+            stack.append(tuple(torch.stack([e[j] for e in ents]) for j in range(3)))
+            del ents
+        else:
+            shape = (K, N) if args.entry == "nt" else (N, K)  # nt: W stored [K, N]
+            w = synth.normal(shape, 0.02, dt, synth.seed_for(2, 0, i), device=dev)
+            stack.append(Q.quantize(w, bits, gs))
+            del w
+    xshape = (lambda M: (NB, M, K)) if args.entry == "batched" else (lambda M: (M, K))
+    yshape = (lambda M: (NB, M, N)) if args.entry == "batched" else (lambda M: (M, N))
+    xs = {M: synth.normal(xshape(M), 1.0, dt, synth.seed_for(2, 1, M), device=dev) for M in Ms}
+    ys = {M: torch.empty(yshape(M), dtype=tdt, device=dev) for M in Ms}
     torch.cuda.synchronize()
 
     # passes over the stack per step and M: at least 32 calls per replayed
@@ -343,14 +373,20 @@ def main():
 
     # --workspace: the workspace entry point (K split across workgroups where
     # its plan says so), with the workspace allocated here, outside the timing
-    wss = {M: torch.empty((max(16, Q.workspace_bytes(tdt, bits, gs, M, N, K)),), dtype=torch.uint8, device=dev)
+    wsb = Q.nt_workspace_bytes if args.entry == "nt" else Q.workspace_bytes
+    wss = {M: torch.empty((max(16, wsb(tdt, bits, gs, M, N, K)),), dtype=torch.uint8, device=dev)
            for M in Ms} if args.workspace else {}
 
     def calls(M):
         x, y = xs[M], ys[M]
         for _ in range(P):
             for (wq, sc, bi) in stack:
-                if args.workspace:
+                if args.entry == "batched":
+                    Q.small_m_batched(x, wq, sc, bi, bits, gs, out=y)
+                elif args.entry == "nt":
+                    Q.small_m_nt(x, wq, sc, bi, bits, gs, out=y, split=args.workspace,
+                                 workspace=wss[M] if args.workspace else None)
+                elif args.workspace:
                     Q.small_m_ws(x, wq, sc, bi, bits, gs, workspace=wss[M], out=y)
                 else:
                     Q.small_m(x, wq, sc, bi, bits, gs, out=y, kernel=args.kernel)
@@ -387,11 +423,14 @@ def main():
     gbs = B * ncalls / (ms * 1e-3) / 1e9
 
     # ---- roofline of the matmul kernel: algorithmic bytes / mean launch duration
-    alg = {M: alg_bytes(M, N, K, bits, gs) for M in Ms}
+    alg = {M: NB * alg_bytes(M, N, K, bits, gs) for M in Ms}
     alg_mean = sum(alg.values()) / len(Ms)
     launch_us = sum(per_m.values()) / len(Ms)
     achieved = alg_mean / (launch_us * 1e-6) / 1e9
     def chosen(M):
+        if args.entry == "nt":
+            sp = Q.nt_workspace_bytes(tdt, bits, gs, M, N, K) // max(1, 4 * M * N) if args.workspace else 0
+            return "nt" + (f" (K split {sp})" if sp > 1 else "")
         if args.workspace:
             k, sp = Q.split_plan(tdt, bits, gs, M, N, K)
             return Q.kernel_name(k) + (f" (K split {sp})" if sp > 1 else "")
@@ -399,7 +438,8 @@ def main():
 
     kid = args.kernel if args.kernel is not None else (
         Q.split_plan(tdt, bits, gs, Ms[-1], N, K)[0] if args.workspace else Q.select_kernel(tdt, bits, gs, Ms[-1], N, K))
-    digest = kernel_source_digest(Q.kernel_name(kid))
+    kname = "nt" if args.entry == "nt" else Q.kernel_name(kid)
+    digest = kernel_source_digest(kname)
     kernels = {f"M{M}": chosen(M) for M in Ms}
 
     extras = {}
@@ -425,25 +465,32 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: M in {list(Ms)}, K={K}, N={N}, {bits}-bit, group {gs}, {dt}; "
-                               f"{S} distinct matrices ({S * B / 2**20:.0f} MiB) cycled per call, "
+                               + (f"{NB} entries per batched call; " if NB > 1 else "")
+                               + (f"weights stored [K, N]; " if args.entry == "nt" else "")
+                               + f"{S} distinct {'weight sets' if NB > 1 else 'matrices'} ({S * B / 2**20:.0f} MiB) cycled per call, "
                                f"{P} pass(es) over them per M per step",
                    "workload_name": args.workload,
-                   "entry": "qmm_small_m_ws" if args.workspace else "qmm_small_m",
+                   "entry": {"batched": "qmm_small_m_batched",
+                             "nt": "qmm_small_m_nt_ws" if args.workspace else "qmm_small_m_nt"}.get(
+                       args.entry, "qmm_small_m_ws" if args.workspace else "qmm_small_m"),
+                   **({"batch": NB} if args.entry == "batched" else {}),
+                   **({"weights": "[K, N], quantized along N"} if args.entry == "nt" else {}),
                    "M": list(Ms), "N": N, "K": K, "bits": bits, "group_size": gs, "stack": S, "passes": P,
                    "kernel": kernels},
         "us_per_call": {f"M{M}": round(per_m[M], 3) for M in Ms},
         "weight_gbs_per_m": {f"M{M}": round(B / (per_m[M] * 1e-6) / 1e9, 1) for M in Ms},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload, digest),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(args.workload, digest) if args.entry == "small_m" else None,
                      "alg_bytes_per_launch": int(alg_mean), "launch_us": round(launch_us, 3),
-                     "kernel": Q.kernel_name(kid)},
+                     "kernel": kname},
         **extras,
         "kernel_source_digest": digest,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(dt, bits, gs, Ms, N, K, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(dt, bits, gs, Ms, N, K, args.cpu_seconds, args.entry)
     print(json.dumps(out), flush=True)
 
 
