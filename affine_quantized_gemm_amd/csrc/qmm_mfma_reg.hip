@@ -857,8 +857,12 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
                           : reg_grid(ntiles, W);
     if (MULTI && !SPLIT && nb > 1) {
         if (ROWS) {
-            grid = reg_rows_grid(RB) / nb / 8 * 8;  // (row blocks of a slot on one XCD)
-            if (grid < 8) grid = 8;
+            // the row blocks of a slot share an XCD when slots x entries is a
+            // multiple of 8 (linear ids then congruent mod 8): the most slots
+            // per entry within the resident workgroups that keep that
+            grid = (256 / RB) / nb;
+            while (grid > 1 && grid * nb % 8 != 0) --grid;
+            if (grid < 1) grid = 1;
         } else {
             grid = 256 * (16 / W) / nb;
             if (grid < 1) grid = 1;
