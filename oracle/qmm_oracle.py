@@ -293,12 +293,6 @@ def qmm_nt(x, wq, scales, biases, dt: str, bits: int, group_size: int, N: int):
     return x64 @ w64, np.abs(x64) @ np.abs(w64)
 
 
-def qmm_columns(x, wq, scales, biases, dt: str, bits: int, group_size: int, cols):
-    """:func:`qmm` restricted to the listed output columns (for sampling)."""
-    cols = np.asarray(cols)
-    return qmm(x, wq[cols], scales[cols], biases[cols], dt, bits, group_size)
-
-
 TOL_REL = 4e-3
 TOL_ABS = 1e-3
 
