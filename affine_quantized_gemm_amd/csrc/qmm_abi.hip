@@ -256,6 +256,14 @@ int64_t qmm_packed_words(int bits, int64_t K) {
     return K * bits / 32;
 }
 
+// The build passes the digest of the sources this library was compiled from
+// (every csrc/ and include/ file); the binding compares it with the sources
+// beside the library before using it.
+#ifndef QMM_SOURCE_DIGEST
+#define QMM_SOURCE_DIGEST "unknown"
+#endif
+const char* qmm_build_digest(void) { return QMM_SOURCE_DIGEST; }
+
 const char* qmm_strerror(int status) {
     switch (status) {
         case QMM_OK: return "ok";

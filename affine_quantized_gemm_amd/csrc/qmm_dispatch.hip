@@ -50,7 +50,8 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
 //   * the VALU kernel is not selected (kept as an independent variant for
 //     measurement and cross-checks).
 // The pages' own dispatch is likewise a measured crossover in M per shape
-// (MLX issue #4720, "Root cause"; crossover near M = 6-8 on Apple parts).
+// (MLX issue #4720: the dispatch rules under "Describe the bug", the
+// crossover near M = 6-8 on Apple parts under "Expected behavior").
 int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     if (kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K)) return QMM_KERNEL_MFMA_REG;
     if (M <= 16) return QMM_KERNEL_MFMA_PASS;

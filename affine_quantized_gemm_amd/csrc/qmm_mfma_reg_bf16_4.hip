@@ -1,0 +1,6 @@
+// Register-kernel launcher for bf16 activations and 4-bit codes (all group sizes).
+#include "qmm_mfma_reg.hpp"
+
+namespace qmm {
+QMM_REG_FMT_LAUNCHER(launch_mfma_reg_bf16_4, DT_BF16, 4)
+}  // namespace qmm

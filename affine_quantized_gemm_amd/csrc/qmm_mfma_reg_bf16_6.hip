@@ -1,0 +1,6 @@
+// Register-kernel launcher for bf16 activations and 6-bit codes (all group sizes).
+#include "qmm_mfma_reg.hpp"
+
+namespace qmm {
+QMM_REG_FMT_LAUNCHER(launch_mfma_reg_bf16_6, DT_BF16, 6)
+}  // namespace qmm

@@ -1,0 +1,6 @@
+// Register-kernel launcher for fp16 activations and 6-bit codes (all group sizes).
+#include "qmm_mfma_reg.hpp"
+
+namespace qmm {
+QMM_REG_FMT_LAUNCHER(launch_mfma_reg_f16_6, DT_F16, 6)
+}  // namespace qmm
