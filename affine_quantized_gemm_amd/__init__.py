@@ -33,6 +33,7 @@ EXPORTS = (
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
     "qmm_small_m_batched", "qmm_small_m_nt", "qmm_small_m_nt_ws", "qmm_small_m_nt_workspace_bytes",
+    "qmm_build_digest",
 )
 
 
@@ -42,11 +43,22 @@ class QmmError(RuntimeError):
         self.status = status
 
 
+class StaleLibraryError(ImportError):
+    """libqmm.so was built from other sources than the ones beside it."""
+
+
 def _load():
+    from . import build as _b
     if not os.path.exists(LIB_PATH):
-        from . import build as _b
         _b.build(verbose=False)
     lib = ctypes.CDLL(LIB_PATH)
+    lib.qmm_build_digest.restype = ctypes.c_char_p
+    lib.qmm_build_digest.argtypes = []
+    built, current = lib.qmm_build_digest().decode(), _b.source_digest()
+    if built != current:
+        raise StaleLibraryError(
+            f"{LIB_PATH} was built from sources with digest {built}, but the sources beside it have digest "
+            f"{current}: rebuild it (python affine_quantized_gemm_amd/build.py)")
     i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
     sig = {
         "qmm_quantize": (i32, [i32, i32, i32, i64, i64, vp, vp, vp, vp, vp]),
@@ -69,6 +81,7 @@ def _load():
         "qmm_small_m_nt": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
         "qmm_small_m_nt_ws": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
         "qmm_small_m_nt_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
+        "qmm_build_digest": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -78,6 +91,7 @@ def _load():
 
 
 _lib = _load()
+BUILD_DIGEST = _lib.qmm_build_digest().decode()
 
 # ---- C entry points under their C names (integer addresses, status codes) ----
 qmm_quantize = _lib.qmm_quantize
@@ -145,13 +159,59 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+_WORD_DTYPES = tuple(d for d in (torch.int32, getattr(torch, "uint32", None)) if d is not None)
+
+
+def _expect(t: torch.Tensor, name: str, shape: tuple, dtypes) -> None:
+    """Shape and dtype of an operand against the problem size (checked before
+    any pointer reaches the library: a wrong bits, group size or buffer would
+    otherwise make the kernels read or write past the tensors)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+
+
+def _words(bits: int, n: int) -> int:
+    """uint32 words per packed row of n codes (QmmError if unsupported)."""
+    w = packed_words(bits, n)
+    if w < 0:
+        raise QmmError(QMM_ERR_UNSUPPORTED, f"bits={bits} with {n} codes per row")
+    return w
+
+
+def _groups(group_size: int, n: int) -> int:
+    if group_size not in (32, 64, 128) or n % group_size:
+        raise QmmError(QMM_ERR_UNSUPPORTED, f"group_size={group_size} with {n} codes per row")
+    return n // group_size
+
+
+def _same_device(ref: torch.Tensor, *named):
+    for t, n in named:
+        if t.device != ref.device:
+            raise ValueError(f"{n} is on {t.device}, expected {ref.device}")
+
+
+def _check_quantized(x_dtype, wq, scales, biases, rows: int, n: int, bits: int, group_size: int,
+                     lead: tuple = ()):
+    """wq [*lead, rows, words(n)], scales / biases [*lead, rows, n/gs] in x's dtype."""
+    _expect(wq, "wq", (*lead, rows, _words(bits, n)), _WORD_DTYPES)
+    g = _groups(group_size, n)
+    _expect(scales, "scales", (*lead, rows, g), (x_dtype,))
+    _expect(biases, "biases", (*lead, rows, g), (x_dtype,))
+
+
 def quantize(w: torch.Tensor, bits: int, group_size: int, stream=None):
     """W [N, K] (fp16/bf16, GPU) -> (wq [N, K*bits/32] int32 words, scales, biases)."""
-    _dev(w, "w")
+    if w.dim() != 2:
+        raise ValueError(f"w must be 2-D [N, K], got shape {tuple(w.shape)}")
+    _dt(w.dtype)
     N, K = w.shape
-    nw = packed_words(bits, K)
-    if nw < 0 or K % group_size:
-        raise QmmError(QMM_ERR_UNSUPPORTED, "quantize shape")
+    nw = _words(bits, K)
+    _groups(group_size, K)
+    _dev(w, "w")
     wq = torch.empty((N, nw), dtype=torch.int32, device=w.device)
     sc = torch.empty((N, K // group_size), dtype=w.dtype, device=w.device)
     bi = torch.empty_like(sc)
@@ -163,10 +223,15 @@ def quantize(w: torch.Tensor, bits: int, group_size: int, stream=None):
 def dequantize(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int, group_size: int,
                stream=None) -> torch.Tensor:
     """(wq, scales, biases) -> W_hat [N, K] in the scales' dtype."""
+    if scales.dim() != 2:
+        raise ValueError(f"scales must be 2-D [N, K/gs], got shape {tuple(scales.shape)}")
+    _dt(scales.dtype)
+    N = scales.shape[0]
+    K = scales.shape[1] * group_size
+    _check_quantized(scales.dtype, wq, scales, biases, N, K, bits, group_size)
     for t, n in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
         _dev(t, n)
-    N = wq.shape[0]
-    K = scales.shape[1] * group_size
+    _same_device(wq, (scales, "scales"), (biases, "biases"))
     out = torch.empty((N, K), dtype=scales.dtype, device=wq.device)
     _check(qmm_dequantize(_dt(scales.dtype), bits, group_size, N, K, wq.data_ptr(), scales.data_ptr(),
                           biases.data_ptr(), out.data_ptr(), _stream(stream)), "qmm_dequantize")
@@ -194,18 +259,34 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     _check(qmm_probe_copy(src.data_ptr(), dst.data_ptr(), nb, _stream(stream)), "qmm_probe_copy")
 
 
+def _check_small_m(x, wq, scales, biases, bits, group_size, out):
+    """Shapes, dtypes and devices of a transposed product; returns (M, K, N)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [M, K], got shape {tuple(x.shape)}")
+    _dt(x.dtype)
+    if wq.dim() != 2:
+        raise ValueError(f"wq must be 2-D [N, K*bits/32], got shape {tuple(wq.shape)}")
+    M, K = x.shape
+    N = wq.shape[0]
+    _check_quantized(x.dtype, wq, scales, biases, N, K, bits, group_size)
+    if out is not None:
+        _expect(out, "out", (M, N), (x.dtype,))
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    _same_device(x, (wq, "wq"), (scales, "scales"), (biases, "biases"))
+    if out is not None:
+        _dev(out, "out")
+        _same_device(x, (out, "out"))
+    return M, K, N
+
+
 def small_m(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
             group_size: int, out: torch.Tensor | None = None, kernel: int | None = None,
             stream=None) -> torch.Tensor:
     """y [M, N] = x [M, K] . dequant(wq, scales, biases)^T (``kernel`` forces a variant)."""
-    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
-        _dev(t, n)
-    M, K = x.shape
-    N = wq.shape[0]
+    M, K, N = _check_small_m(x, wq, scales, biases, bits, group_size, out)
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    else:
-        _dev(out, "out")
     args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
             biases.data_ptr(), out.data_ptr(), _stream(stream))
     if kernel is None:
@@ -219,16 +300,24 @@ def small_m_batched(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, bia
                     group_size: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y [B, M, N]: y[b] = x[b] . dequant(wq[b], scales[b], biases[b])^T, one weight set per entry
     (x [B, M, K], wq [B, N, words], scales / biases [B, N, K/gs])."""
-    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
-        _dev(t, n)
+    if x.dim() != 3:
+        raise ValueError(f"x must be 3-D [B, M, K], got shape {tuple(x.shape)}")
+    _dt(x.dtype)
+    if wq.dim() != 3:
+        raise ValueError(f"wq must be 3-D [B, N, K*bits/32], got shape {tuple(wq.shape)}")
     B, M, K = x.shape
     N = wq.shape[1]
-    if wq.shape[0] != B or scales.shape[0] != B or biases.shape[0] != B:
-        raise ValueError("x, wq, scales and biases need the same batch size")
+    _check_quantized(x.dtype, wq, scales, biases, N, K, bits, group_size, lead=(B,))
+    if out is not None:
+        _expect(out, "out", (B, M, N), (x.dtype,))
+    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, n)
+    _same_device(x, (wq, "wq"), (scales, "scales"), (biases, "biases"))
     if out is None:
         out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
     else:
         _dev(out, "out")
+        _same_device(x, (out, "out"))
     _check(qmm_small_m_batched(_dt(x.dtype), bits, group_size, B, M, N, K, x.data_ptr(), wq.data_ptr(),
                                scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
            "qmm_small_m_batched")
@@ -248,16 +337,26 @@ def small_m_nt(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
                workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] = x [M, K] . dequant(W) for W stored [K, N] and quantized along N
     (wq [K, N*bits/32], scales / biases [K, N/gs]: :func:`quantize` of a [K, N] matrix)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [M, K], got shape {tuple(x.shape)}")
+    _dt(x.dtype)
+    if wq.dim() != 2:
+        raise ValueError(f"wq must be 2-D [K, N*bits/32], got shape {tuple(wq.shape)}")
+    if bits not in (4, 6, 8):
+        raise QmmError(QMM_ERR_UNSUPPORTED, f"bits={bits}")
+    M, K = x.shape
+    N = wq.shape[1] * 32 // bits
+    _check_quantized(x.dtype, wq, scales, biases, K, N, bits, group_size)
+    if out is not None:
+        _expect(out, "out", (M, N), (x.dtype,))
     for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
         _dev(t, n)
-    M, K = x.shape
-    if wq.shape[0] != K:
-        raise ValueError("wq needs one row per column of x")
-    N = wq.shape[1] * 32 // bits
+    _same_device(x, (wq, "wq"), (scales, "scales"), (biases, "biases"))
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
         _dev(out, "out")
+        _same_device(x, (out, "out"))
     args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
             biases.data_ptr(), out.data_ptr())
     if not split:
@@ -295,19 +394,15 @@ def small_m_ws(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
     """As :func:`small_m`, K possibly split across workgroups with fp32 partial
     outputs in ``workspace`` (a device tensor the caller keeps; allocated here
     when not given).  ``kernel`` and ``split`` force the variant and split."""
-    for t, n in ((x, "x"), (wq, "wq"), (scales, "scales"), (biases, "biases")):
-        _dev(t, n)
-    M, K = x.shape
-    N = wq.shape[0]
+    M, K, N = _check_small_m(x, wq, scales, biases, bits, group_size, out)
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    else:
-        _dev(out, "out")
     if workspace is None:
         need = workspace_bytes(x.dtype, bits, group_size, M, N, K) if kernel is None else \
             max(1, int(split or 1)) * M * N * 4
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace")
+    _same_device(x, (workspace, "workspace"))
     nb = workspace.numel() * workspace.element_size()
     args = (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(), scales.data_ptr(),
             biases.data_ptr(), out.data_ptr(), workspace.data_ptr(), nb, _stream(stream))

@@ -173,7 +173,9 @@ int qmm_small_m_nt_ws(int dt, int bits, int group_size, int64_t M, int64_t N, in
                       const void* x, const uint32_t* wq, const void* scales, const void* biases,
                       void* y, void* workspace, int64_t workspace_bytes, void* stream);
 
-/* As qmm_small_m with the variant forced (measurement and tests).
+/* As qmm_small_m with the variant forced (measurement and tests): the
+ * counterpart of timing qmm_nax forced against the stock dispatch in MLX
+ * issue #4720, "Expected behavior".
  * QMM_ERR_UNSUPPORTED if the variant cannot run this shape
  * (QMM_KERNEL_MFMA_REG needs K <= 4096; for M = 17..64 it runs on 16-row
  * blocks and needs K to fill 16 wavefronts with whole k-blocks (above 1024
@@ -192,7 +194,7 @@ int qmm_small_m_forced(int dt, int bits, int group_size, int64_t M, int64_t N, i
  * its columns; with K split S ways a CU reads 1/S of it.  The partial
  * outputs (fp32, [S][M][N]) go to a caller-provided workspace and a second
  * kernel adds them in split order and rounds once, so results stay
- * deterministic.  This splits K the way MLX issue #4720 ("Root cause")
+ * deterministic.  This splits K the way MLX issue #4720 ("Describe the bug")
  * describes qmm_splitk; there it is the slow path on Apple parts, here it is
  * taken only where it measured faster.
  *
@@ -233,7 +235,11 @@ int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64
                    int* kernel_id, int* split);
 
 /* The variant qmm_small_m runs for this problem (a qmm_kernel value), or a
- * negative status if the problem is not supported.  Pure host logic. */
+ * negative status if the problem is not supported.  Pure host logic.  The
+ * selection is a table of measured crossovers over (dt, bits, group size, M,
+ * N, K): MLX issue #4720 shows a dispatch keyed on M and N (its qmv cutoff
+ * and split_k rule, "Describe the bug") misrouting shapes whose crossover
+ * lies elsewhere ("Expected behavior": near M = 6-8 on 4096-class shapes). */
 int qmm_select_kernel(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K);
 
 /* 1 if variant `kernel_id` can run this problem, 0 if it cannot, or a
@@ -244,6 +250,11 @@ int qmm_kernel_supported(int dt, int bits, int group_size, int64_t M, int64_t N,
 /* uint32 words per packed row: K*bits/32 (-1 for unsupported bits or a K
  * that does not fill whole words). */
 int64_t qmm_packed_words(int bits, int64_t K);
+
+/* Hex digest (SHA-256, first 16 digits) of the source files this library
+ * was built from, or "unknown" for a build that did not record it; callers
+ * compare it with the sources they ship to detect a stale binary. */
+const char* qmm_build_digest(void);
 
 /* Static description of a status code. */
 const char* qmm_strerror(int status);
