@@ -18,7 +18,9 @@ per M, the sum of the seven calls with the variant qmm_small_m selects, and
 with qmm_small_m_ws's plan where it takes a split.
 
 The pages' own dispatch story is a crossover curve in M, measured per shape
-(MLX issue #4720, "Root cause" and the M-sweep table under "Measurements").
+(MLX issue #4720: the dispatch rules and the split_k rule under "Describe the
+bug", the per-M GB/s of forced qmm_nax and the M = 6-8 crossover under
+"Expected behavior").
 """
 
 from __future__ import annotations
