@@ -87,6 +87,7 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
 // 64.
 SplitPlan plan_split(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
     SplitPlan p{select_kernel(dt, bits, gs, M, N, K), 1};
+    if (M < 1 || N < 1) return p;  // empty problem: nothing to split
     if (p.kernel == QMM_KERNEL_MFMA_REG && !(M > 48 && mfma_reg_single_tile_rows(bits, gs, M, N, K)))
         return p;  // faster than any split measured
     if (!mfma_reg_supports(bits, gs, 1, N, K))  // K deeper than the register kernel takes whole

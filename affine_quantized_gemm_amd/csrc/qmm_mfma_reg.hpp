@@ -956,7 +956,7 @@ hipError_t launch_shape(const MatmulArgs& a) {
 // of K / split (and, above 16 rows, 16-row blocks), each (slice, row block)
 // with 256 / (split x blocks) workgroups walking more column tiles than that.
 inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, int split, RegShape& s) {
-    if (bits != 4 || M > 64 || split < 2 || K % split != 0) return false;
+    if (bits != 4 || M < 1 || M > 64 || split < 2 || K % split != 0) return false;
     if (!pick_shape(bits, gs, K / split, s) || !s.vec || s.W != 16) return false;
     const int64_t ntiles = (N + 15) / 16;
     const int64_t per = 256 * (16 / s.W) / (split * ((M + 15) / 16));  // resident workgroups per (slice, block)

@@ -371,3 +371,14 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stderr)
     assert r.stdout.strip() == Q.kernel_name(Q.KERNEL_MFMA_REG)
+
+
+def test_empty_problem_plans():
+    """Workspace size and split plan of an empty problem (M = 0 or N = 0):
+    no split, no workspace (the plan's per-row-block arithmetic is never
+    reached with zero rows)."""
+    for M, N in ((0, 4096), (4, 0), (0, 0)):
+        assert Q.qmm_small_m_workspace_bytes(0, 4, 64, M, N, 14336) == 0
+        kid, split = ctypes.c_int(-1), ctypes.c_int(-1)
+        assert Q._lib.qmm_split_plan(0, 4, 64, M, N, 14336, ctypes.byref(kid), ctypes.byref(split)) == Q.QMM_OK
+        assert split.value == 1
