@@ -33,8 +33,9 @@ EXPORTS = (
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
     "qmm_small_m_batched", "qmm_small_m_nt", "qmm_small_m_nt_ws", "qmm_small_m_nt_workspace_bytes",
-    "qmm_build_digest",
+    "qmm_build_digest", "qmm_small_m_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024  # QMM_NOALLOC_SCRATCH_BYTES
 
 
 class QmmError(RuntimeError):
@@ -82,6 +83,7 @@ def _load():
         "qmm_small_m_nt_ws": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
         "qmm_small_m_nt_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
         "qmm_build_digest": (ctypes.c_char_p, []),
+        "qmm_small_m_noalloc": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -111,6 +113,7 @@ qmm_small_m_batched = _lib.qmm_small_m_batched
 qmm_small_m_nt = _lib.qmm_small_m_nt
 qmm_small_m_nt_ws = _lib.qmm_small_m_nt_ws
 qmm_small_m_nt_workspace_bytes = _lib.qmm_small_m_nt_workspace_bytes
+qmm_small_m_noalloc = _lib.qmm_small_m_noalloc
 
 
 def strerror(status: int) -> str:
@@ -411,4 +414,19 @@ def small_m_ws(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
     else:
         kid = kernel if kernel is not None else split_plan(x.dtype, bits, group_size, M, N, K)[0]
         _check(qmm_small_m_split_forced(*args, int(kid), int(split or 1)), "qmm_small_m_split_forced")
+    return out
+
+
+def small_m_noalloc(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+                    group_size: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """As :func:`small_m_ws` with its own plan, the K-split partials in the
+    library's static per-GPU scratch instead of a workspace (the call itself
+    allocates nothing when ``out`` is given).  Calls that overlap on one GPU
+    race on that scratch."""
+    M, K, N = _check_small_m(x, wq, scales, biases, bits, group_size, out)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(qmm_small_m_noalloc(_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wq.data_ptr(),
+                               scales.data_ptr(), biases.data_ptr(), out.data_ptr(), _stream(stream)),
+           "qmm_small_m_noalloc")
     return out

@@ -234,6 +234,29 @@ int qmm_small_m_split_forced(int dt, int bits, int group_size, int64_t M, int64_
 int qmm_split_plan(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
                    int* kernel_id, int* split);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP stream or
+ * graph capture, serving loops and harnesses that forbid hipMalloc):
+ * exactly qmm_small_m_ws -- the same plan, kernels and results -- with the
+ * workspace in a library-owned static device array of
+ * QMM_NOALLOC_SCRATCH_BYTES per GPU instead of a caller buffer.  Nothing is
+ * allocated by the call (the array is part of the loaded library; each GPU
+ * the library runs on holds its own copy until the process ends; its
+ * address is looked up once per device, at the first call on it).
+ *   - A problem whose planned workspace (qmm_small_m_workspace_bytes)
+ *     exceeds QMM_NOALLOC_SCRATCH_BYTES -> QMM_ERR_UNSUPPORTED, checked
+ *     before any HIP call; use qmm_small_m_ws with a caller buffer there.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's partial sums: calls that overlap on one GPU (two streams, two
+ *     threads) race and must be ordered by the caller.  Sequential calls
+ *     need no clearing (each split overwrites the partials it reads).
+ * Otherwise as qmm_small_m.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+int qmm_small_m_noalloc(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K,
+                        const void* x, const uint32_t* wq, const void* scales,
+                        const void* biases, void* y, void* stream);
+
 /* The variant qmm_small_m runs for this problem (a qmm_kernel value), or a
  * negative status if the problem is not supported.  Pure host logic.  The
  * selection is a table of measured crossovers over (dt, bits, group size, M,

@@ -373,6 +373,30 @@ int main(void) {
     assert r.stdout.strip() == Q.kernel_name(Q.KERNEL_MFMA_REG)
 
 
+def test_noalloc_validation():
+    """qmm_small_m_noalloc rejects bad arguments and problems whose planned
+    workspace exceeds its static scratch before any HIP call."""
+    K = 14336
+
+    def na(dt=0, bits=4, gs=64, M=16, N=4096, x=A, wq=A, s=A, b=A, y=A):
+        return Q.qmm_small_m_noalloc(dt, bits, gs, M, N, K, x, wq, s, b, y, None)
+
+    assert Q.NOALLOC_SCRATCH_BYTES == 8 * 1024 * 1024
+    assert na(M=-1) == Q.QMM_ERR_INVALID_ARG
+    assert na(bits=5) == Q.QMM_ERR_UNSUPPORTED
+    assert na(M=65) == Q.QMM_ERR_UNSUPPORTED
+    assert na(M=0, x=None, y=None) == Q.QMM_OK
+    assert na(N=0, x=None, y=None) == Q.QMM_OK
+    # planned workspace above the scratch: refused
+    big = Q.qmm_small_m_workspace_bytes(0, 4, 64, 16, 32768, K)
+    assert big > Q.NOALLOC_SCRATCH_BYTES
+    assert na(N=32768) == Q.QMM_ERR_UNSUPPORTED
+    # within it, but bad pointers
+    assert 0 < Q.qmm_small_m_workspace_bytes(0, 4, 64, 16, 4096, K) <= Q.NOALLOC_SCRATCH_BYTES
+    assert na(x=None) == Q.QMM_ERR_INVALID_ARG
+    assert na(y=MIS) == Q.QMM_ERR_MISALIGNED
+
+
 def test_empty_problem_plans():
     """Workspace size and split plan of an empty problem (M = 0 or N = 0):
     no split, no workspace (the plan's per-row-block arithmetic is never
