@@ -18,11 +18,27 @@ Metric: effective weight GB/s = (packed weight bytes + 4 bytes of scale and
 bias per group) / time per call, GB = 1e9 bytes -- the byte count of the
 MLX issue #4720 reproducer ("To Reproduce").  Printed as one JSON line.
 
+The default run also measures every workload of the method's benchmark
+set in one ``configs`` sub-record (``--no-configs`` skips it): the tiny
+verify case, verify at the stated 32-matrix stack, the batched-decode sweep
+(down and gate/up projections, split-free and with the K-split workspace
+plan), the precision matrix at M = 6 (bits x group size x dtype at N = 1024
+and 4096, and the 1%-outlier variant) and the wide LM head (4- and 8-bit).
+Per workload and M: graph-replayed us/call, effective weight GB/s, roofline
+fraction, the kernel chosen, the streaming-read ceiling at the same byte
+count and a short oracle timing on the host.
+
 Counter post-processing (no GPU): ``bench.py --traffic-from FETCH_DIR
 WRITE_DIR`` reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
 runs of this script, scales the matmul kernel's counters by what the same
 counters read for the copy-kernel dispatch of known size that every run
 makes, and writes ``profiles/traffic_<workload>.json``.
+
+Trace post-processing (no GPU): ``bench.py --summarize-trace DIR CMD``
+reads a ``rocprofv3 --kernel-trace`` run of ``bench.py --timed-only`` (which
+launches nothing but the timed graph replays after its warm-up) and writes
+``profiles/<kernel>_<workload>_kernel_stats.md``: the per-dispatch durations
+of the timed region's matmul kernels, against the bench line of that run.
 """
 
 from __future__ import annotations
@@ -85,6 +101,13 @@ def parse():
                    help="skip the graph-replay and streaming-read measurements")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="post-process two rocprofv3 --pmc runs of this script (no GPU)")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-config sub-record")
+    p.add_argument("--config-steps", type=int, default=5, help="timed graph replays per M in the sub-record")
+    p.add_argument("--timed-only", action="store_true",
+                   help="launch nothing but the warm-up and timed graph replays (and one copy-kernel "
+                        "dispatch for the byte counters): for profiler runs")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                   help="post-process a rocprofv3 --kernel-trace run of --timed-only (no GPU)")
     return p.parse_args()
 
 
@@ -93,10 +116,10 @@ def parse():
 # these are unchanged.
 KERNEL_SOURCES = {
     "valu_splitfree": ["qmm_valu.hip"],
-    "mfma_splitfree_reg": ["qmm_mfma_reg.hip", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_reg": ["qmm_mfma_reg.hpp", "qmm_mfma_frag.hpp"],
     "mfma_splitfree_pass": ["qmm_mfma_pass.hip", "qmm_mfma_frag.hpp"],
-    "mfma_splitfree_tile16": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
-    "mfma_splitfree_tile64": ["qmm_mfma_tile.hip", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_tile16": ["qmm_mfma_tile.hpp", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_tile64": ["qmm_mfma_tile.hpp", "qmm_mfma_frag.hpp"],
     "nt": ["qmm_nt.hip", "qmm_mfma_frag.hpp"],
 }
 COMMON_SOURCES = ["qmm_device.hpp", "qmm_internal.hpp"]
@@ -214,6 +237,7 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s, entry="small_m"):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    host_cores = len(os.sched_getaffinity(0))
     Ns = min(N, 16384)
     if entry == "nt":  # weights [K, N] quantized along N: the whole matrix
         Ns = N
@@ -241,7 +265,7 @@ def cpu_baseline(dt, bits, gs, Ms, N, K, budget_s, entry="small_m"):
               + f", {el:.1f} s; {per_call * 1e6:.0f} us per full call")
     return {"value": round(weight_bytes(N, K, bits, gs) / per_call / 1e9, 4), "unit": "GB/s",
             "cores": int(threads), "kind": "oracle", "sample": sample,
-            "us_per_call": round(per_call * 1e6, 1)}
+            "us_per_call": round(per_call * 1e6, 1), "host_cores": host_cores, "blas_threads": int(threads)}
 
 
 # ---------------------------------------------------------------- GPU legs
@@ -320,10 +344,211 @@ def copy_calibration(torch, Q):
         raise RuntimeError("probe copy mismatch")
 
 
+# ---------------------------------------------------------------- per-config sub-record
+
+KSHORT = {"valu_splitfree": "valu", "mfma_splitfree_reg": "reg", "mfma_splitfree_pass": "pass",
+          "mfma_splitfree_tile16": "tile16", "mfma_splitfree_tile64": "tile64"}
+
+
+def config_cells():
+    """(key, dtype, bits, gs, Ms, N, K, entry, wstd, outlier, stack) of every
+    workload in the benchmark set; stack None = >= --stack-mib of distinct
+    matrices, an int = that many matrices."""
+    cells = [("c1_tiny", "f16", 4, 64, (4,), 512, 512, "small_m", 1.0, 0.0, 1),
+             ("c2_verify_stack32", "f16", 4, 64, (4, 6), 4096, 4096, "small_m", 0.02, 0.0, 32)]
+    dec = (8, 16, 32, 36, 48, 64)
+    for name, N, K in (("down", 4096, 14336), ("gateup", 14336, 4096)):
+        cells.append((f"c3_{name}", "f16", 4, 64, dec, N, K, "small_m", 0.02, 0.0, None))
+        cells.append((f"c3_{name}_ws", "f16", 4, 64, dec, N, K, "ws", 0.02, 0.0, None))
+    for dt in ("f16", "bf16"):
+        for bits in (4, 6, 8):
+            for gs in (32, 64, 128):
+                for N in (1024, 4096):
+                    cells.append((f"c4_{dt}_{bits}b_gs{gs}_N{N}", dt, bits, gs, (6,), N, 4096, "small_m", 0.02, 0.0,
+                                  None))
+                cells.append((f"c4_{dt}_{bits}b_gs{gs}_N1024_outlier", dt, bits, gs, (6,), 1024, 4096, "small_m",
+                              0.02, 0.01, None))
+    cells.append(("c5_lmhead4", "bf16", 4, 64, (4, 6), 151936, 4096, "small_m", 0.02, 0.0, None))
+    cells.append(("c5_lmhead8", "bf16", 8, 64, (4, 6), 151936, 4096, "small_m", 0.02, 0.0, None))
+    return cells
+
+
+def oracle_us_per_call(dt, bits, gs, M, N, K, wstd, rows=512, seed=9300):
+    """One untuned oracle call (unpack, fp64 dequant, fp64 matmul) on the
+    first min(N, rows) output columns, scaled to all N (columns are
+    independent); the quantization is not timed."""
+    import synth
+    from oracle import qmm_oracle as O
+    Ns = min(N, rows)
+    w = synth.to_oracle(synth.normal((Ns, K), wstd, dt, seed))
+    wq, sc, bi = O.quantize(w, dt, bits, gs)
+    x = synth.to_oracle(synth.normal((M, K), 1.0, dt, seed + 1))
+    best = None
+    for _ in range(2):
+        t = time.perf_counter()
+        O.qmm(x, wq, sc, bi, dt, bits, gs)
+        el = time.perf_counter() - t
+        best = el if best is None else min(best, el)
+    return best * 1e6 * N / Ns
+
+
+def measure_cell(torch, Q, synth, cell, steps, warmup, stack_mib, ceilings):
+    """Graph-replayed timing of one workload of the benchmark set (the same
+    protocol as the headline: distinct quantized matrices cycled call by
+    call, at least 32 calls per replayed graph, events around each replay)."""
+    key, dt, bits, gs, Ms, N, K, entry, wstd, outlier, stack = cell
+    tdt = synth.TORCH_DT[dt]
+    dev = torch.device("cuda:0")
+    B = weight_bytes(N, K, bits, gs)
+    S = stack if stack is not None else max(1, -(-(stack_mib << 20) // B))
+    mats = []
+    for i in range(S):
+        w = synth.normal((N, K), wstd, dt, 20000 + 7 * i, device=dev, outlier_frac=outlier)
+        mats.append(Q.quantize(w, bits, gs))
+        del w
+    P = max(1, -(-32 // S))
+    xs = {M: synth.normal((M, K), 1.0, dt, 20500 + M, device=dev) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=tdt, device=dev) for M in Ms}
+    wss = {M: torch.empty((max(16, Q.workspace_bytes(tdt, bits, gs, M, N, K)),), dtype=torch.uint8, device=dev)
+           for M in Ms} if entry == "ws" else {}
+
+    def calls(M):
+        for _ in range(P):
+            for (wq, sc, bi) in mats:
+                if entry == "ws":
+                    Q.small_m_ws(xs[M], wq, sc, bi, bits, gs, workspace=wss[M], out=ys[M])
+                else:
+                    Q.small_m(xs[M], wq, sc, bi, bits, gs, out=ys[M])
+
+    us, kern = [], []
+    for M in Ms:
+        g = capture(torch, lambda M=M: calls(M))
+        for _ in range(warmup):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / (steps * S * P))
+        del g
+        if entry == "ws":
+            k, sp = Q.split_plan(tdt, bits, gs, M, N, K)
+            kern.append(KSHORT[Q.kernel_name(k)] + (f"/split{sp}" if sp > 1 else ""))
+        else:
+            kern.append(KSHORT[Q.kernel_name(Q.select_kernel(tdt, bits, gs, M, N, K))])
+    del mats, xs, ys, wss
+    if B not in ceilings and stack is None:
+        ceilings[B] = stream_read_ceiling(torch, Q, B, S * B, max(2, steps))["us_per_call"]
+    ceil = ceilings.get(B)
+    rec = {"M": list(Ms), "us": [round(u, 3) for u in us],
+           "gbs": [round(B / (u * 1e-6) / 1e9, 1) for u in us],
+           "frac": [round(alg_bytes(M, N, K, bits, gs) / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for M, u in zip(Ms, us)],
+           "kernel": kern, "stack": S}
+    if ceil is not None:
+        rec["ceil_us"] = ceil
+        rec["of_ceil"] = [round(ceil / u, 3) for u in us]
+    rec["oracle_us"] = round(oracle_us_per_call(dt, bits, gs, Ms[-1], N, K, wstd), 0)
+    return rec
+
+
+def empty_kernel_period(torch, Q, reps=20):
+    """Graph-replayed back-to-back period of a near-empty kernel (one
+    workgroup reading 16 bytes): the launch floor under any kernel here."""
+    src = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+
+    def launches():
+        for _ in range(64):
+            Q.probe_stream_read(src, sink, 1, 0)
+    g = capture(torch, launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / (reps * 64), 3)
+
+
+def run_configs(torch, Q, synth, steps, stack_mib):
+    t0 = time.perf_counter()
+    ceilings = {}
+    out = {}
+    for cell in config_cells():
+        out[cell[0]] = measure_cell(torch, Q, synth, cell, steps, 2, stack_mib, ceilings)
+        torch.cuda.empty_cache()
+        print(f"config {cell[0]}: {out[cell[0]]['us']} us", file=sys.stderr, flush=True)
+    out["wall_s"] = round(time.perf_counter() - t0, 1)
+    return out
+
+
+# ---------------------------------------------------------------- trace summary
+
+def summarize_trace(trace_dir, command):
+    """Per-dispatch durations of the timed region of a --timed-only run
+    under rocprofv3 --kernel-trace, against the bench line of that run."""
+    line = _bench_line(trace_dir)
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if _is_matmul_kernel(name):
+                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    rows.sort()
+    n_timed = line["timed_dispatches"]
+    main_rows = [r for r in rows if "reduce_partials" not in r[2]]
+    timed = main_rows[-n_timed:]
+    t_lo = timed[0][0]
+    red = [r for r in rows if "reduce_partials" in r[2] and r[0] >= t_lo]
+    per = {}
+    for a, b, name in timed + red:
+        per.setdefault(name, []).append((b - a) / 1e3)
+    short = lambda n: n.split("(")[0].replace("(anonymous namespace)::", "")
+    calls_per_step = n_timed / line["steps"]
+    wl, kname = line["config"]["workload_name"], line["roofline"]["kernel"]
+    main_name = max((n for n in per if "reduce_partials" not in n), key=lambda n: len(per[n]))
+    avg_main = sum(sum(v) for n, v in per.items() if "reduce_partials" not in n) / n_timed
+    lines = [f"# rocprofv3 kernel trace, timed region only: {wl} workload", "",
+             "Command (from the repository root):", "", "    cd /tmp && export TMPDIR=/tmp && cd -",
+             f"    {command}", "",
+             f"Dispatches of the timed region: the last {n_timed} matmul-kernel dispatches of the run "
+             f"({line['steps']} steps x {calls_per_step:.0f} calls; the run launches nothing else after "
+             "its warm-up but one copy kernel). Durations from the trace's start and end stamps.", "",
+             "| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        vs = sorted(v)
+        lines.append(f"| `{short(name)}` | {len(v)} | {sum(v) / len(v):.3f} | {vs[len(vs) // 2]:.3f} | "
+                     f"{vs[0]:.3f} | {vs[-1]:.3f} |")
+    alg = line["roofline"]["alg_bytes_per_launch"]
+    lines += ["", "Against the bench line of the same run (events around each graph replay, profiler attached):", "",
+              f"- ms_per_step {line['ms_per_step']}; us_per_call {json.dumps(line['us_per_call'])}",
+              f"- matmul kernels: {avg_main:.3f} us average x {calls_per_step:.0f} calls per step = "
+              f"{avg_main * calls_per_step / 1e3:.4f} ms of the {line['ms_per_step']} ms step",
+              f"- roofline from the trace: {alg} algorithmic bytes per launch / {avg_main:.3f} us = "
+              f"{alg / (avg_main * 1e-6) / 1e9:.1f} GB/s = frac {alg / (avg_main * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} "
+              f"(the line's event-timed frac: {line['roofline']['frac']})",
+              f"- kernel_source_digest {line['kernel_source_digest']}", ""]
+    name = kname if kname == "nt" else KSHORT.get(kname, kname)
+    path = os.path.join(ROOT, "profiles", f"{kname}_{wl}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {path} ({name}: {avg_main:.3f} us avg over {n_timed} timed dispatches)")
+
+
 def main():
     args = parse()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -442,8 +667,16 @@ def main():
     digest = kernel_source_digest(kname)
     kernels = {f"M{M}": chosen(M) for M in Ms}
 
+    # matmul-kernel dispatches of the timed region (a batched call that the
+    # register kernel does not take is one launch per entry)
+    per_call = 1
+    if args.entry == "batched" and any(Q.select_kernel(tdt, bits, gs, M, N, K) != Q.KERNEL_MFMA_REG for M in Ms):
+        per_call = NB
+    timed_dispatches = args.steps * S * P * len(Ms) * per_call
+
     extras = {}
-    if not args.no_extras:
+    if not args.no_extras and not args.timed_only:
+        extras["empty_kernel_period_us"] = empty_kernel_period(torch, Q)
         extras["stream_launched_us_per_call"] = {
             f"M{M}": round(stream_us_per_call(torch, lambda M=M: calls(M), S * P, max(2, args.steps // 4)), 3)
             for M in Ms}
@@ -487,9 +720,15 @@ def main():
                      "kernel": kname},
         **extras,
         "kernel_source_digest": digest,
+        "library_build_digest": Q.BUILD_DIGEST,
+        "timed_dispatches": timed_dispatches,
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
+    default_run = (args.workload == "verify" and args.entry == "small_m" and args.kernel is None
+                   and not args.workspace)
+    if default_run and not args.no_configs and not args.timed_only:
+        out["configs"] = run_configs(torch, Q, synth, args.config_steps, args.stack_mib)
+    if not args.no_cpu_baseline and not args.timed_only:
         out["cpu_baseline"] = cpu_baseline(dt, bits, gs, Ms, N, K, args.cpu_seconds, args.entry)
     print(json.dumps(out), flush=True)
 
