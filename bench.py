@@ -106,8 +106,12 @@ def parse():
     p.add_argument("--timed-only", action="store_true",
                    help="launch nothing but the warm-up and timed graph replays (and one copy-kernel "
                         "dispatch for the byte counters): for profiler runs")
-    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
-                   help="post-process a rocprofv3 --kernel-trace run of --timed-only (no GPU)")
+    p.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                   help="TRACE_DIR COMMAND [REFERENCE_LOG]: post-process a rocprofv3 --kernel-trace run of "
+                        "--timed-only, against the bench line of an unprofiled run of the same workload (no GPU)")
+    p.add_argument("--summarize-util", nargs="+", metavar="PMC_DIR",
+                   help="post-process rocprofv3 --pmc MfmaUtil VALUBusy runs of --timed-only into "
+                        "profiles/mfma_valu_utilization.md (no GPU)")
     return p.parse_args()
 
 
@@ -179,6 +183,37 @@ def _read_counter_dir(d, counter):
     return name, sum(vals) / len(vals), len(vals), sum(copies) / len(copies)
 
 
+def _labelled_dispatches(d, counter, line):
+    """The matmul-kernel dispatches of a --timed-only run under --pmc, in
+    launch order, each labelled with its M from the run's launch sequence
+    (per M: S*P eager calls then one capture replay; then warm-up and timed
+    replays, M after M).  None if the count does not match that sequence."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    rows = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and _is_matmul_kernel(r["Kernel_Name"]):
+                    rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    c = line["config"]
+    Ms, SP = line["us_per_call"].keys(), c["stack"] * c["passes"]
+    Ms = [int(k[1:]) for k in Ms]
+    seq = []
+    for M in Ms:
+        seq += [M] * (2 * SP)
+    for _ in range(line["warmup"] + line["steps"]):
+        for M in Ms:
+            seq += [M] * SP
+    ids = sorted(rows)
+    if len(ids) != len(seq):
+        return None
+    return [(M, rows[i][0], rows[i][1]) for M, i in zip(seq, ids)]
+
+
+def _short_kernel(name):
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void qmm::", "")
+
+
 def _bench_line(d):
     for fn in glob.glob(os.path.join(d, "*.log")) + glob.glob(os.path.join(d, "*.json")):
         with open(fn) as f:
@@ -216,6 +251,21 @@ def traffic_from(fetch_dir, write_dir):
         "alg_bytes_per_launch": bf["roofline"]["alg_bytes_per_launch"],
         "traffic_over_alg": round((fetch_b + write_b) / bf["roofline"]["alg_bytes_per_launch"], 4),
     }
+    # per M (decode sweeps run several kernels): mean bytes per dispatch
+    lf = _labelled_dispatches(fetch_dir, "FETCH_SIZE", bf)
+    lw = _labelled_dispatches(write_dir, "WRITE_SIZE", bw)
+    if lf and lw:
+        c = bf["config"]
+        per_m = {}
+        for M in sorted({m for m, _, _ in lf}):
+            fv = [v for m, _, v in lf if m == M]
+            wv = [v for m, _, v in lw if m == M]
+            names = sorted({_short_kernel(n) for m, n, _ in lf if m == M})
+            hbm = (sum(fv) / len(fv)) * 1024.0 * f_scale + (sum(wv) / len(wv)) * 1024.0 * w_scale
+            alg = alg_bytes(M, c["N"], c["K"], c["bits"], c["group_size"])
+            per_m[f"M{M}"] = {"kernel": names, "hbm_bytes_per_launch": int(hbm), "alg_bytes_per_launch": alg,
+                              "traffic_over_alg": round(hbm / alg, 4)}
+        out["per_m"] = per_m
     path = os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -485,11 +535,53 @@ def run_configs(torch, Q, synth, steps, stack_mib):
     return out
 
 
+# ---------------------------------------------------------------- utilisation summary
+
+def summarize_util(dirs):
+    """MfmaUtil and VALUBusy (rocprofv3's derived counters) per workload, M
+    and kernel, mean over every dispatch of that M in each run."""
+    lines = ["# Matrix-core and vector-ALU utilization (rocprofv3 derived counters)", "",
+             "Commands (from the repository root), one run per workload:", "",
+             "    cd /tmp && export TMPDIR=/tmp && cd -"]
+    rows = []
+    for d in dirs:
+        line = _bench_line(d)
+        wl = line["config"]["workload_name"]
+        lines.append(f"    rocprofv3 --pmc MfmaUtil VALUBusy -d {d} -o run --output-format csv -- python3 bench.py "
+                     f"--workload {wl} --timed-only --steps {line['steps']} --warmup {line['warmup']}")
+        mu = _labelled_dispatches(d, "MfmaUtil", line)
+        vb = _labelled_dispatches(d, "VALUBusy", line)
+        if not mu or not vb:
+            raise SystemExit(f"{d}: dispatches do not match the run's launch sequence")
+        for M in sorted({m for m, _, _ in mu}):
+            a = [v for m, _, v in mu if m == M]
+            b = [v for m, _, v in vb if m == M]
+            names = ", ".join(sorted({_short_kernel(n) for m, n, _ in mu if m == M}))
+            rows.append(f"| {wl} | {M} | `{names}` | {len(a)} | {sum(a) / len(a):.1f} | {sum(b) / len(b):.1f} |")
+    lines += ["", "`MfmaUtil` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) x 100; `VALUBusy` = "
+              "SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE x 100 (rocprofv3's definitions).  Mean over the "
+              "dispatches of each M in the run (eager, capture replay, warm-up and timed calls).", "",
+              "| workload | M | kernel | dispatches | MfmaUtil % | VALUBusy % |", "|---|---|---|---|---|---|", *rows, ""]
+    path = os.path.join(ROOT, "profiles", "mfma_valu_utilization.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {path}")
+
+
 # ---------------------------------------------------------------- trace summary
 
-def summarize_trace(trace_dir, command):
+def _line_in(path):
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("{") and '"metric"' in ln:
+                return json.loads(ln)
+    raise SystemExit(f"no bench JSON line in {path}")
+
+
+def summarize_trace(trace_dir, command, reference=None):
     """Per-dispatch durations of the timed region of a --timed-only run
-    under rocprofv3 --kernel-trace, against the bench line of that run."""
+    under rocprofv3 --kernel-trace, against the bench line of that run and,
+    if given, of an unprofiled run of the same workload."""
     line = _bench_line(trace_dir)
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
@@ -510,7 +602,7 @@ def summarize_trace(trace_dir, command):
     per = {}
     for a, b, name in timed + red:
         per.setdefault(name, []).append((b - a) / 1e3)
-    short = lambda n: n.split("(")[0].replace("(anonymous namespace)::", "")
+    short = _short_kernel
     calls_per_step = n_timed / line["steps"]
     wl, kname = line["config"]["workload_name"], line["roofline"]["kernel"]
     main_name = max((n for n in per if "reduce_partials" not in n), key=lambda n: len(per[n]))
@@ -535,6 +627,23 @@ def summarize_trace(trace_dir, command):
               f"{alg / (avg_main * 1e-6) / 1e9:.1f} GB/s = frac {alg / (avg_main * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} "
               f"(the line's event-timed frac: {line['roofline']['frac']})",
               f"- kernel_source_digest {line['kernel_source_digest']}", ""]
+    if reference:
+        ref = _line_in(reference)
+        if ref["config"] != line["config"] or ref["kernel_source_digest"] != line["kernel_source_digest"]:
+            raise SystemExit("the reference line is of another workload or other kernel sources")
+        ref_frac = ref["roofline"]["frac"]
+        tr_frac = alg / (avg_main * 1e-6) / 1e9 / HBM_PEAK_GBS
+        lines += ["Against the bench line of an unprofiled run of the same workload and sources "
+                  f"(`{reference}`):", "",
+                  f"- ms_per_step {ref['ms_per_step']}; us_per_call {json.dumps(ref['us_per_call'])}; "
+                  f"launch_us {ref['roofline']['launch_us']}",
+                  f"- kernels from the trace x calls per step = {avg_main * calls_per_step / 1e3:.4f} ms "
+                  f"against its {ref['ms_per_step']} ms step (ratio "
+                  f"{avg_main * calls_per_step / 1e3 / ref['ms_per_step']:.3f}: below 1 the gaps between launches, "
+                  "and for a split call its reduction pass; above 1 the tracer's lengthening of each dispatch)",
+                  f"- roofline frac from the trace {tr_frac:.4f} against the line's {ref_frac} "
+                  f"({(tr_frac / ref_frac - 1) * 100:+.1f} %; the line divides by the whole call, the trace by "
+                  "the matmul kernel alone)", ""]
     name = kname if kname == "nt" else KSHORT.get(kname, kname)
     path = os.path.join(ROOT, "profiles", f"{kname}_{wl}_kernel_stats.md")
     with open(path, "w") as f:
@@ -549,6 +658,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_util:
+        summarize_util(args.summarize_util)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
