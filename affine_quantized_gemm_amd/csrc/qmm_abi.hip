@@ -165,7 +165,7 @@ int64_t qmm_small_m_nt_workspace_bytes(int dt, int bits, int group_size, int64_t
     int st = check_format(dt, bits, group_size, K, N);
     if (st != QMM_OK) return st;
     if (M > 64 || K < 32 || K % 32 != 0) return QMM_ERR_UNSUPPORTED;
-    const qmm::NtPlan p = qmm::nt_plan(M, N, K);
+    const qmm::NtPlan p = qmm::nt_plan(bits, M, N, K);
     return p.split > 1 ? static_cast<int64_t>(p.split) * M * N * 4 : 0;
 }
 

@@ -35,6 +35,10 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
 //     1024 x 4096 k/v projection; 8-bit K = N = 4096: 12.0 / 16.5 / 21.6 us
 //     vs 17.3 / 19.9 / 27.9 us (16-column tiles) at M = 24 / 36 / 64, 6-bit
 //     gs128 11.8 / 16.6 / 22.5 us vs 17.2 (pass) / 20.0 / 29.0 us;
+//     Except 6/8-bit at group size 32 above 48 rows (N = 4096): there the
+//     register kernel's 8 units per wavefront make the 16-column tile
+//     kernel faster (22.8-23.8 us vs 24.3-25.6 us at M = 64, all four
+//     formats; sweep.py --formats);
 //   * otherwise (6/8-bit with more tiles than resident workgroups), M > 16,
 //     wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
 //     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
@@ -53,6 +57,9 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
 // (MLX issue #4720: the dispatch rules under "Describe the bug", the
 // crossover near M = 6-8 on Apple parts under "Expected behavior").
 int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
+    if (bits != 4 && gs == 32 && M > 48 && N >= 4096 && mfma_reg_single_tile_rows(bits, gs, M, N, K) &&
+        kernel_supports(QMM_KERNEL_MFMA_TILE16, dt, bits, gs, M, N, K))
+        return QMM_KERNEL_MFMA_TILE16;
     if (kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K)) return QMM_KERNEL_MFMA_REG;
     if (M <= 16) return QMM_KERNEL_MFMA_PASS;
     if (kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) {

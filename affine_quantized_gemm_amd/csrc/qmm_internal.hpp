@@ -60,8 +60,9 @@ struct NtPlan {
     bool wide;   // 128-column workgroups
     int split;   // K slices (1: unsplit, no workspace)
     int64_t ks;  // rows per slice (a multiple of 32)
+    bool tr;     // the transpose-read form (4- and 8-bit codes)
 };
-NtPlan nt_plan(int64_t M, int64_t N, int64_t K);
+NtPlan nt_plan(int bits, int64_t M, int64_t N, int64_t K);
 hipError_t launch_nt_split(const MatmulArgs& a);
 // M <= 16: every format where the k-blocks fit; M 17..64, on 16-row blocks
 // (vector form, 16 wavefronts): 4-bit LDS-ring grids on shapes with more

@@ -483,22 +483,313 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Transpose-read form (4- and 8-bit codes).  gfx950's LDS transpose reads
+// deliver exactly the operand the matrix cores want from rows of packed codes:
+// within each group of 16 lanes, ds_read_b64_tr_b4 gives lane i nibble i of
+// the 8-byte blocks the 16 lanes address (lane i receives 16 codes of one
+// column from 16 rows), and ds_read_b64_tr_b8 gives lane i byte i % 8 of the
+// blocks of lanes 2j + i / 8, j = 0..7 (8 rows of one column when lanes 2j,
+// 2j + 1 address the two 8-column halves of row j).  (Layouts checked on the
+// hardware.)  So the weights go global -> LDS as whole row pieces with
+// 16-byte coalesced loads, and each 16-column tile's B operand comes out of
+// LDS already transposed: no cross-lane shuffles at all.
+//
+// Workgroup: 4 wavefronts own a block of 128 columns (8 tiles, 2 per
+// wavefront) and one slice of K (blockIdx.y), walked in chunks of 16 KiB of
+// weights (256 rows at 4 bits, 128 at 8) staged in LDS; the next chunk's
+// weights, activations and scales are loaded into registers while the
+// current one is computed.  A wavefront's tiles are its own for the whole
+// slice, so there is no combine: it stores fp32 partials part[slice][M][N]
+// (several slices; a second kernel adds them in slice order) or, with one
+// slice, rounds and stores y.
+//
+// Rows past the end of the slice inside the last 64-row (32-row) block keep
+// whatever codes the LDS holds but get scale and bias 0 (so w = 0) and zero
+// activations.
+constexpr int NTT_BN = 128;        // columns per workgroup
+constexpr int NTT_THREADS = 256;   // 4 wavefronts, 2 tiles each
+constexpr int NTT_CHUNK_BYTES = 16384;
+constexpr int NTT_GMAX = NTT_BN / 32;  // groups a block spans at most
+
+template <int BITS>
+struct NttFmt {
+    static constexpr int RP = NTT_BN * BITS / 8;              // bytes of a row piece (64 / 128)
+    static constexpr int KC = NTT_CHUNK_BYTES / RP;           // rows per chunk (256 / 128)
+    static constexpr int BLK = BITS == 4 ? 64 : 32;           // rows per transpose read (16 / 8 per lane group)
+    static constexpr int CPR = RP / 16;                       // 16-byte pieces per row
+    static constexpr int WPT = NTT_CHUNK_BYTES / 16 / NTT_THREADS;  // weight pieces per thread (4)
+    static constexpr int XS = KC + 8;                         // activation row stride in LDS (elements)
+    // LDS position of 16-byte piece c of row r (swizzled so that the
+    // transpose reads of 16 consecutive rows spread over the banks)
+    __device__ static constexpr int swz(int r) { return BITS == 4 ? ((r >> 1) & 3) : (r & 7); }
+};
+
+template <int DT, int BITS, int RB, bool PART>
+__global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ part, int M, int64_t N,
+    int64_t K, int gs, int64_t kr) {
+    using F = NttFmt<BITS>;
+    constexpr int KC = F::KC, XS = F::XS, BLK = F::BLK;
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t* const w_lds = lds;                                                       // [KC][RP], swizzled
+    uint16_t* const x_lds = reinterpret_cast<uint16_t*>(lds + NTT_CHUNK_BYTES);        // [16 RB][XS]
+    uint16_t* const s_lds = x_lds + 16 * RB * XS;                                      // [GMAX][KC]
+    uint16_t* const b_lds = s_lds + NTT_GMAX * KC;                                     // [GMAX][KC]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, q = lane >> 4;
+    // 4-bit: a 128-byte weight line holds 256 columns, two column blocks.
+    // Workgroups whose linear ids differ by 8 run on one XCD; the two blocks
+    // of a line are given such a pair (when the grid allows), so that the
+    // line comes from HBM once and from that XCD's L2 the second time.
+    int bx = static_cast<int>(blockIdx.x), by = static_cast<int>(blockIdx.y);
+    {
+        const int cb = static_cast<int>(gridDim.x), tot = cb * static_cast<int>(gridDim.y);
+        if (BITS == 4 && cb % 2 == 0 && tot % 16 == 0) {
+            const int L = bx + cb * by;
+            const int P = (L & 7) + 8 * (L >> 4), h = (L >> 3) & 1;
+            bx = 2 * (P % (cb / 2)) + h;
+            by = P / (cb / 2);
+        }
+    }
+    const int64_t n0 = static_cast<int64_t>(bx) * NTT_BN;
+    const int ncols = static_cast<int>(N - n0 < NTT_BN ? N - n0 : NTT_BN);  // 64 or 128
+    const int64_t k_lo = static_cast<int64_t>(by) * kr;
+    const int64_t k_hi = k_lo + kr < K ? k_lo + kr : K;
+    const int64_t G = N / gs;
+    const int64_t g0 = n0 / gs;
+    const int gw = (ncols + gs - 1) / gs;  // groups of this block (1..4)
+    const int64_t row_bytes = N * BITS / 8;
+    const uint8_t* const wbase = reinterpret_cast<const uint8_t*>(wq) + n0 * BITS / 8;
+
+    // activation rows M .. 16 RB - 1 stay zero for the whole kernel
+    for (int i = tid; i < (16 * RB - M) * XS; i += NTT_THREADS) x_lds[M * XS + i] = 0;
+
+    // register prefetch of one chunk
+    uint4 wv[F::WPT];
+    constexpr int XPT = (16 * RB * KC / 8 + NTT_THREADS - 1) / NTT_THREADS;  // activation pieces per thread
+    uint4 xv[XPT];
+    uint16_t sv[NTT_GMAX], bv[NTT_GMAX];
+    auto load_chunk = [&](int64_t kc0) __attribute__((always_inline)) {
+        const int rows = static_cast<int>(k_hi - kc0 < KC ? k_hi - kc0 : KC);
+#pragma unroll
+        for (int i = 0; i < F::WPT; ++i) {
+            const int p = tid + NTT_THREADS * i;
+            const int r = p / F::CPR, c = (p % F::CPR) ^ F::swz(r);
+            if (r < rows && c * 16 * 8 / BITS < ncols)
+                wv[i] = *reinterpret_cast<const uint4*>(wbase + (kc0 + r) * row_bytes + c * 16);
+        }
+        const int cpr = KC / 8;  // activation pieces per row
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int p = tid + NTT_THREADS * i;
+            const int m = p / cpr, c = p % cpr;
+            xv[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (m < M && 8 * c < rows) xv[i] = *reinterpret_cast<const uint4*>(x + m * K + kc0 + 8 * c);
+        }
+        if (tid < KC) {
+#pragma unroll
+            for (int g = 0; g < NTT_GMAX; ++g) {
+                sv[g] = bv[g] = 0;
+                if (g < gw && tid < rows) {
+                    sv[g] = scales[(kc0 + tid) * G + g0 + g];
+                    bv[g] = biases[(kc0 + tid) * G + g0 + g];
+                }
+            }
+        }
+    };
+    auto stage_chunk = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < F::WPT; ++i) *reinterpret_cast<uint4*>(w_lds + 16 * (tid + NTT_THREADS * i)) = wv[i];
+        const int cpr = KC / 8;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int p = tid + NTT_THREADS * i;
+            const int m = p / cpr, c = p % cpr;
+            if (m < M) *reinterpret_cast<uint4*>(x_lds + m * XS + 8 * c) = xv[i];
+        }
+        if (tid < KC) {
+#pragma unroll
+            for (int g = 0; g < NTT_GMAX; ++g) {
+                s_lds[g * KC + tid] = sv[g];
+                b_lds[g * KC + tid] = bv[g];
+            }
+        }
+    };
+
+    float4_t acc[2][RB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[t][b] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int t0 = 2 * wave;                      // this wavefront's tiles: t0, t0 + 1
+    const bool live = 16 * t0 < ncols;            // (uniform: a 64-column block has tiles 0..3)
+    const int gt = 16 * t0 / gs;                  // the two tiles' group (gs >= 32)
+
+    load_chunk(k_lo);
+    for (int64_t kc0 = k_lo; kc0 < k_hi; kc0 += KC) {
+        stage_chunk();
+        __syncthreads();
+        if (kc0 + KC < k_hi) load_chunk(kc0 + KC);  // in flight during the compute below
+        const int rows = static_cast<int>(k_hi - kc0 < KC ? k_hi - kc0 : KC);
+        if (live) {
+            for (int blk = 0; blk < rows; blk += BLK) {
+                // scales and biases of this lane's rows (quarter q), for the tiles' group
+                constexpr int SUB = BLK / 32;  // MFMA steps per transpose read (2 at 4 bits, 1 at 8)
+                uint32_t sw[SUB][4], bw[SUB][4];
+#pragma unroll
+                for (int st = 0; st < SUB; ++st) {
+                    const int r0 = blk + (BITS == 4 ? 16 * q + 8 * st : 8 * q);
+                    const uint4 s4 = *reinterpret_cast<const uint4*>(s_lds + gt * KC + r0);
+                    const uint4 b4 = *reinterpret_cast<const uint4*>(b_lds + gt * KC + r0);
+                    sw[st][0] = s4.x; sw[st][1] = s4.y; sw[st][2] = s4.z; sw[st][3] = s4.w;
+                    bw[st][0] = b4.x; bw[st][1] = b4.y; bw[st][2] = b4.z; bw[st][3] = b4.w;
+                }
+                // activation fragments: rows 16 b + li, the same k positions
+                Frag xa[SUB][RB];
+#pragma unroll
+                for (int st = 0; st < SUB; ++st)
+#pragma unroll
+                    for (int b = 0; b < RB; ++b) {
+                        const int k = blk + (BITS == 4 ? 16 * q + 8 * st : 8 * q);
+                        const uint4 v = *reinterpret_cast<const uint4*>(x_lds + (16 * b + li) * XS + k);
+                        xa[st][b].v[0] = v.x; xa[st][b].v[1] = v.y; xa[st][b].v[2] = v.z; xa[st][b].v[3] = v.w;
+                    }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int t = t0 + tt;
+                    // transpose read: lane (q, li) addresses one 8-byte block
+                    int r, off;
+                    if constexpr (BITS == 4) {
+                        r = blk + 16 * q + li;                               // 16 rows per lane group
+                        off = ((t >> 1) ^ F::swz(r)) * 16 + (t & 1) * 8;     // tile t's 8 bytes (16 codes)
+                    } else {
+                        r = blk + 8 * q + (li >> 1);                         // 8 rows, two halves each
+                        off = (t ^ F::swz(r)) * 16 + (li & 1) * 8;
+                    }
+                    typedef int v2i_t __attribute__((ext_vector_type(2)));
+                    auto* pa = reinterpret_cast<__attribute__((address_space(3))) v2i_t*>(
+                        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(w_lds)) + r * F::RP + off);
+                    v2i_t tr;
+                    if constexpr (BITS == 4)
+                        tr = __builtin_amdgcn_ds_read_tr4_b64_v2i32(pa);
+                    else
+                        tr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(pa);
+#pragma unroll
+                    for (int st = 0; st < SUB; ++st) {
+                        Frag wh, wl;
+                        if constexpr (BITS == 4)  // nibbles of rows 8 st .. 8 st + 7 (of this quarter's 16)
+                            dequant_frags<DT, 4>(static_cast<uint32_t>(tr[st]), 0u, sw[st], bw[st], wh, wl);
+                        else                      // bytes of rows 0..3 and 4..7
+                            dequant_frags<DT, 8>(static_cast<uint32_t>(tr[0]), static_cast<uint32_t>(tr[1]), sw[st],
+                                                 bw[st], wh, wl);
+#pragma unroll
+                        for (int b = 0; b < RB; ++b) {
+                            acc[tt][b] = mf::mfma<DT>(xa[st][b], wh, acc[tt][b]);
+                            if constexpr (DT == DT_BF16) acc[tt][b] = mf::mfma<DT>(xa[st][b], wl, acc[tt][b]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the chunk's LDS is overwritten next
+    }
+
+    if (!live) return;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int m = 16 * b + 4 * q + rr;
+                const int64_t n = n0 + 16 * (t0 + tt) + li;
+                if (m < M) {
+                    if constexpr (PART)
+                        part[(static_cast<int64_t>(by) * M + m) * N + n] = acc[tt][b][rr];
+                    else
+                        y[static_cast<int64_t>(m) * N + n] = DtOps<DT>::rne(acc[tt][b][rr]);
+                }
+            }
+}
+
+template <int BITS, int RB>
+constexpr size_t ntt_lds_bytes() {
+    return NTT_CHUNK_BYTES + 2 * (16 * RB * NttFmt<BITS>::XS + 2 * NTT_GMAX * NttFmt<BITS>::KC);
+}
+
+template <int DT, int BITS, int RB, bool PART>
+hipError_t launch_nt_tr_t(const MatmulArgs& a, int split, int64_t kr) {
+    constexpr size_t lds = ntt_lds_bytes<BITS, RB>();
+    if (lds > 65536) {
+        static std::atomic<uint64_t> raised{0};
+        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&nt_tr_kernel<DT, BITS, RB, PART>), raised);
+            e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((nt_tr_kernel<DT, BITS, RB, PART>),
+                       dim3(static_cast<unsigned>((a.N + NTT_BN - 1) / NTT_BN), static_cast<unsigned>(split)),
+                       dim3(NTT_THREADS), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
+                       static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
+                       static_cast<uint16_t*>(a.y), a.part, static_cast<int>(a.M), a.N, a.K, a.gs, kr);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if constexpr (PART) return launch_reduce_partials(DT, a.part, a.y, split, a.M * a.N, a.stream);
+    return hipSuccess;
+}
+
+template <int DT, int BITS>
+hipError_t launch_nt_tr_b(const MatmulArgs& a, int split, int64_t kr) {
+    const bool p = split > 1;
+    switch ((a.M + 15) / 16) {
+        case 1: return p ? launch_nt_tr_t<DT, BITS, 1, true>(a, split, kr) : launch_nt_tr_t<DT, BITS, 1, false>(a, split, kr);
+        case 2: return p ? launch_nt_tr_t<DT, BITS, 2, true>(a, split, kr) : launch_nt_tr_t<DT, BITS, 2, false>(a, split, kr);
+        case 3: return p ? launch_nt_tr_t<DT, BITS, 3, true>(a, split, kr) : launch_nt_tr_t<DT, BITS, 3, false>(a, split, kr);
+        case 4: return p ? launch_nt_tr_t<DT, BITS, 4, true>(a, split, kr) : launch_nt_tr_t<DT, BITS, 4, false>(a, split, kr);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_nt_tr(const MatmulArgs& a, int split, int64_t kr) {
+    switch (a.dt * 10 + a.bits) {
+        case 4: return launch_nt_tr_b<DT_F16, 4>(a, split, kr);
+        case 8: return launch_nt_tr_b<DT_F16, 8>(a, split, kr);
+        case 14: return launch_nt_tr_b<DT_BF16, 4>(a, split, kr);
+        case 18: return launch_nt_tr_b<DT_BF16, 8>(a, split, kr);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 // K split of the workspace entry point: 128-column workgroups, slices enough
 // for about 256 workgroups (at most 16, at least 2 steps of 32 rows each);
 // wide N (>= 128 such workgroups) runs unsplit.
-NtPlan nt_plan(int64_t M, int64_t N, int64_t K) {
+NtPlan nt_plan(int bits, int64_t M, int64_t N, int64_t K) {
     (void)M;
-    NtPlan p{false, 1, K};
     const int64_t groups = (N + 127) / 128;  // 128-column workgroups
-    if (groups >= 128) return NtPlan{true, 1, K};  // wide N: enough workgroups unsplit
+    if (bits != 6 && groups >= 32) {
+        // transpose-read form: about 512 workgroups (two per CU), slices of
+        // whole 32-row steps, at most 16 (the partial sums grow with the
+        // slices; with fewer than 32 column blocks, e.g. N = 1024, the
+        // 16-wavefront form below fills the chip with fewer slices)
+        if (groups >= 256) return NtPlan{true, 1, K, true};
+        int64_t split = (512 + groups / 2) / groups;
+        if (split > 16) split = 16;
+        if (split > K / 32) split = K / 32;
+        if (split < 2) return NtPlan{true, 1, K, true};
+        const int64_t ks = ((K + split - 1) / split + 31) / 32 * 32;
+        return NtPlan{true, static_cast<int>((K + ks - 1) / ks), ks, true};
+    }
+    NtPlan p{false, 1, K, false};
+    if (groups >= 128) return NtPlan{true, 1, K, false};  // wide N: enough workgroups unsplit
     int64_t split = 256 / groups;
     if (split > 16) split = 16;
     if (split > K / 64) split = K / 64;
     if (split < 2) return p;
     const int64_t ks = ((K + split - 1) / split + 31) / 32 * 32;  // rows per slice, whole 32-row steps
-    return NtPlan{true, static_cast<int>((K + ks - 1) / ks), ks};
+    return NtPlan{true, static_cast<int>((K + ks - 1) / ks), ks, false};
 }
 
 namespace {
@@ -511,6 +802,8 @@ bool nt_shape_ok(const MatmulArgs& a) {
 hipError_t launch_nt(const MatmulArgs& a) {
     // shapes the kernels assume (validated by the caller)
     if (!nt_shape_ok(a)) return hipErrorInvalidValue;
+    // wide N: the transpose-read form (4/8-bit) unsplit
+    if (a.bits != 6 && (a.N + 127) / 128 >= 256) return launch_nt_tr(a, 1, a.K);
     if ((a.N + 127) / 128 >= 128) {  // wide N: the 128-column form, unsplit
         switch (a.dt * 10 + a.bits) {
             case 4: return launch_nt_wide_b<DT_F16, 4>(a, 1, a.K);
@@ -535,9 +828,10 @@ hipError_t launch_nt(const MatmulArgs& a) {
 
 hipError_t launch_nt_split(const MatmulArgs& a) {
     if (!nt_shape_ok(a)) return hipErrorInvalidValue;
-    const NtPlan p = nt_plan(a.M, a.N, a.K);
+    const NtPlan p = nt_plan(a.bits, a.M, a.N, a.K);
     if (p.split < 2) return launch_nt(a);
     if (a.part == nullptr) return hipErrorInvalidValue;
+    if (p.tr) return launch_nt_tr(a, p.split, p.ks);
     switch (a.dt * 10 + a.bits) {
         case 4: return launch_nt_wide_b<DT_F16, 4>(a, p.split, p.ks);
         case 6: return launch_nt_wide_b<DT_F16, 6>(a, p.split, p.ks);

@@ -9,6 +9,7 @@ variant per (shape, M) is what ``qmm_select_kernel`` should return; the
 measured table is the source of the crossovers compiled into the dispatch.
 
     python -m affine_quantized_gemm_amd.sweep [--json out.json] [--shapes verify,kv,...] [--splits] [--layer]
+    python -m affine_quantized_gemm_amd.sweep --formats [--json out.json] [--markdown table.md]
 
 ``--layer`` adds a synthetic decoder layer at the page's projection shapes
 (hidden 4096, intermediate 14336: q and o 4096 -> 4096, k and v 4096 -> 1024,
@@ -87,8 +88,8 @@ def time_calls(fn, n_calls, reps=5):
 SPLITS = ((3, 2), (3, 4), (4, 2), (4, 4), (4, 8), (1, 2), (1, 4), (1, 7))
 
 
-def sweep_shape(name, ms, stack_mib, splits=False):
-    N, K, dt, bits, gs = SHAPES[name]
+def sweep_shape(name, ms, stack_mib, splits=False, shape=None, kernels=None):
+    N, K, dt, bits, gs = shape if shape is not None else SHAPES[name]
     tdt = synth.TORCH_DT[dt]
     B = weight_bytes(N, K, bits, gs)
     S = max(2, -(-(stack_mib << 20) // B))
@@ -102,7 +103,7 @@ def sweep_shape(name, ms, stack_mib, splits=False):
         x = synth.normal((M, K), 1.0, dt, 7500 + M, device="cuda")
         y = torch.empty((M, N), dtype=tdt, device="cuda")
         res = {}
-        for kid in Q.KERNEL_IDS:
+        for kid in (kernels if kernels is not None else Q.KERNEL_IDS):
             if not Q.kernel_supported(tdt, bits, gs, M, N, K, kid):
                 continue
 
@@ -146,6 +147,54 @@ def sweep_shape(name, ms, stack_mib, splits=False):
     del stack
     torch.cuda.empty_cache()
     return rows
+
+
+# --formats: every format of the precision matrix at K = 4096, N = 1024 and
+# 4096, and the 6/8-bit formats at wide N (gate/up-like 14336 columns) above
+# 16 rows, where the choice among the MFMA variants changes.  The VALU
+# variant, which the table never selects, is left out.
+FORMAT_MS = (1, 4, 6, 8, 16, 24, 36, 64)
+WIDE_MS = (24, 36, 64)
+MFMA_KERNELS = (1, 2, 3, 4)
+
+
+def format_shapes():
+    out = []
+    for dt in ("f16", "bf16"):
+        for bits in (4, 6, 8):
+            for gs in (32, 64, 128):
+                for N in (1024, 4096):
+                    out.append((f"{dt}-{bits}b-gs{gs}-N{N}", (N, 4096, dt, bits, gs), FORMAT_MS))
+                if bits != 4:
+                    out.append((f"{dt}-{bits}b-gs{gs}-N14336", (14336, 4096, dt, bits, gs), WIDE_MS))
+    return out
+
+
+def selection_margin(rows):
+    """Per row, how much slower the selected variant is than the fastest
+    (1.0 = the fastest)."""
+    return [r["us"][r["selected"]] / r["us"][r["fastest"]] for r in rows]
+
+
+def markdown_table(rows, title, command):
+    """The sweep rows as a markdown table (variants in id order)."""
+    names = [Q.kernel_name(k) for k in Q.KERNEL_IDS]
+    short = {n: n.replace("mfma_splitfree_", "").replace("valu_splitfree", "valu") for n in names}
+    used = [n for n in names if any(n in r["us"] for r in rows)]
+    lines = [f"# {title}", "", "Command (from the repository root):", "", f"    {command}", "",
+             "us per call, best of 5 replays of a HIP graph cycling a >= 576 MiB stack of distinct quantized "
+             "matrices (weights stream from HBM); `-` = the variant cannot run the shape.  `selected` is what "
+             "qmm_select_kernel returns, `sel/fastest` its time over the fastest variant's.", "",
+             "| shape | N x K | M | " + " | ".join(short[n] for n in used) + " | fastest | selected | sel/fastest |",
+             "|---|---|---|" + "---|" * len(used) + "---|---|---|"]
+    for r in rows:
+        cells = " | ".join(f"{r['us'][n]:.2f}" if n in r["us"] else "-" for n in used)
+        lines.append(f"| {r['shape']} | {r['N']} x {r['K']} | {r['M']} | {cells} | {short[r['fastest']]} | "
+                     f"{short[r['selected']]} | {r['us'][r['selected']] / r['us'][r['fastest']]:.3f} |")
+    m = selection_margin(rows)
+    lines += ["", f"{len(rows)} rows; the selection is the fastest in {sum(1 for v in m if v == 1.0)}, within 5 % of "
+              f"it in {sum(1 for v in m if v <= 1.05)}, worst {max(m):.3f}.", ""]
+    return "\n".join(lines)
 
 
 # (shape, calls per layer): q, o -> verify; k, v -> kv; gate, up -> gateup; down
@@ -277,12 +326,30 @@ def main():
     p.add_argument("--batched", action="store_true", help="also time the batched entry point")
     p.add_argument("--nt", action="store_true", help="also time non-transposed weights")
     p.add_argument("--nt-shapes", default=",".join(NT_SHAPES), help="shapes for --nt")
+    p.add_argument("--formats", action="store_true",
+                   help="sweep every format of the precision matrix (MFMA variants only) instead of --shapes")
+    p.add_argument("--markdown", default=None, help="also write the rows as a markdown table to this path")
     a = p.parse_args()
     ms = [int(m) for m in a.ms.split(",")]
     shapes = [s for s in a.shapes.split(",") if s]
     if a.layer:
         shapes += [name for name, _ in LAYER if name not in shapes]
     rows = []
+    if a.formats:
+        for name, shape, fms in format_shapes():
+            rows += sweep_shape(name, fms, a.stack_mib, shape=shape, kernels=MFMA_KERNELS)
+        if a.markdown:
+            with open(a.markdown, "w") as f:
+                f.write(markdown_table(rows, "Kernel crossover sweep over every format (MI355X)",
+                                       "python3 -m affine_quantized_gemm_amd.sweep --formats --json "
+                                       "gpurun_out/sweep_formats.json --markdown gpurun_out/dispatch_formats.md"))
+        if a.json:
+            with open(a.json, "w") as f:
+                json.dump(rows, f, indent=1)
+        m = selection_margin(rows)
+        print(f"{len(rows)} rows: selection fastest in {sum(1 for v in m if v == 1.0)}, within 5 % in "
+              f"{sum(1 for v in m if v <= 1.05)}, worst {max(m):.3f}", flush=True)
+        return
     for name in shapes:
         rows += sweep_shape(name, ms, a.stack_mib, a.splits)
     out = rows

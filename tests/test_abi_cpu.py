@@ -193,6 +193,42 @@ def test_dispatch_follows_measured_crossovers():
         # K that is not a whole number of 4-bit k-blocks: the pass kernel
         assert sel(f16, 4, 64, M, 14336, 4160) == "mfma_splitfree_pass"
     assert sel(f16, 6, 64, 40, 4096, 4160) == "mfma_splitfree_tile16"   # 6-bit k-blocks are 64 codes
+    # 6/8-bit at group size 32 above 48 rows: the 16-column tile kernel (sweep.py --formats)
+    for dt in (f16, bf16):
+        for b in (6, 8):
+            assert sel(dt, b, 32, 64, 4096, 4096) == "mfma_splitfree_tile16"
+            assert sel(dt, b, 32, 48, 4096, 4096) == "mfma_splitfree_reg"
+            assert sel(dt, b, 64, 64, 4096, 4096) == "mfma_splitfree_reg"
+
+
+def test_dispatch_matches_the_format_sweep():
+    """Every (format, shape, M) row measured by sweep.py --formats (committed
+    in profiles/dispatch_formats.md): the variant qmm_select_kernel returns
+    now is within 5 % of the fastest measured one."""
+    import torch
+    rows = []
+    with open(os.path.join(ROOT, "profiles", "dispatch_formats.md")) as f:
+        lines = [l for l in f if l.startswith("| ") and not l.startswith("| shape") and "---" not in l]
+    header = None
+    with open(os.path.join(ROOT, "profiles", "dispatch_formats.md")) as f:
+        for l in f:
+            if l.startswith("| shape"):
+                header = [c.strip() for c in l.strip().strip("|").split("|")]
+    assert header and len(lines) == 324
+    names = {"reg": 1, "pass": 2, "tile16": 3, "tile64": 4}
+    dts = {"f16": torch.float16, "bf16": torch.bfloat16}
+    worst = 0.0
+    for l in lines:
+        c = dict(zip(header, [v.strip() for v in l.strip().strip("|").split("|")]))
+        dt, bits, gs, _ = c["shape"].split("-")
+        N, K = (int(v) for v in c["N x K"].split(" x "))
+        M = int(c["M"])
+        times = {k: float(c[k]) for k in names if c.get(k, "-") != "-"}
+        sel = Q.kernel_name(Q.select_kernel(dts[dt], int(bits[:-1]), int(gs[2:]), M, N, K)).replace(
+            "mfma_splitfree_", "")
+        worst = max(worst, times[sel] / min(times.values()))
+        assert times[sel] <= 1.05 * min(times.values()), (c["shape"], M, sel, times)
+    assert worst <= 1.05
 
 
 def test_split_plan_and_workspace_bytes():
@@ -316,22 +352,29 @@ def test_nt_validation():
 
 
 def test_nt_split_plan_and_validation():
-    """qmm_small_m_nt_ws: 128-column workgroups with K slices for about 256
-    workgroups (at most 16); unsplit where N gives 128 such workgroups or K
-    is short; errors before any HIP call."""
-    f16 = Q.QMM_F16
+    """qmm_small_m_nt_ws: 128-column workgroups with K slices.  4/8-bit with
+    at least 32 column blocks (the transpose-read form): about 512
+    workgroups, at most 16 slices, unsplit from 256 blocks; otherwise (6-bit,
+    or N below 4096) the 16-wavefront form: about 256 workgroups, at most 16
+    slices, unsplit from 128 blocks; unsplit when K is short; errors before
+    any HIP call."""
+    f16, bf16 = Q.QMM_F16, Q.QMM_BF16
     wb = Q.qmm_small_m_nt_workspace_bytes
-    assert wb(f16, 4, 64, 6, 4096, 4096) == 8 * 6 * 4096 * 4       # 32 workgroups x 8 slices
-    assert wb(f16, 4, 64, 6, 1024, 4096) == 16 * 6 * 1024 * 4      # capped at 16 slices
-    assert wb(f16, 4, 64, 4, 4096, 14336) == 8 * 4 * 4096 * 4
+    assert wb(f16, 4, 64, 6, 4096, 4096) == 16 * 6 * 4096 * 4      # 32 blocks x 16 slices (transpose reads)
+    assert wb(bf16, 8, 32, 6, 4096, 4096) == 16 * 6 * 4096 * 4
+    assert wb(f16, 6, 64, 6, 4096, 4096) == 8 * 6 * 4096 * 4       # 6-bit: 32 x 8 slices
+    assert wb(f16, 4, 64, 6, 1024, 4096) == 16 * 6 * 1024 * 4      # 8 blocks: the 16-wavefront form, 16 slices
+    assert wb(f16, 4, 64, 4, 4096, 14336) == 16 * 4 * 4096 * 4
+    assert wb(f16, 4, 64, 6, 14336, 4096) == 5 * 6 * 14336 * 4     # 112 blocks x 5 slices
     assert wb(f16, 4, 64, 64, 1024, 4160) == 15 * 64 * 1024 * 4    # slices of 288 rows, the last shorter
-    assert wb(f16, 4, 64, 6, 16384, 4096) == 0                     # 128 workgroups: unsplit
+    assert wb(f16, 6, 64, 6, 16384, 4096) == 0                     # 6-bit, 128 blocks: unsplit
+    assert wb(f16, 4, 64, 6, 32768, 4096) == 0                     # 256 blocks: unsplit
     assert wb(f16, 4, 64, 6, 256, 96) == 0                         # one slice of K
     assert wb(f16, 4, 64, -1, 256, 96) == Q.QMM_ERR_INVALID_ARG
     assert wb(f16, 4, 64, 6, 96, 96) == Q.QMM_ERR_UNSUPPORTED
     ws = Q.qmm_small_m_nt_ws
     base = (f16, 4, 64, 6, 4096, 4096, A, A, A, A, A)
-    need = 8 * 6 * 4096 * 4
+    need = 16 * 6 * 4096 * 4
     assert ws(*base, A, need - 4, None) == Q.QMM_ERR_INVALID_ARG
     assert ws(*base, None, need, None) == Q.QMM_ERR_INVALID_ARG
     assert ws(*base, MIS, need, None) == Q.QMM_ERR_MISALIGNED
@@ -358,7 +401,7 @@ int main(void) {
     if (qmm_select_kernel(QMM_F16, 4, 64, 6, 4096, 4096) != QMM_KERNEL_MFMA_REG) return 2;
     if (qmm_small_m(QMM_F16, 5, 64, 4, 64, 256, 0, 0, 0, 0, 0, 0) != QMM_ERR_UNSUPPORTED) return 3;
     if (qmm_split_plan(QMM_F16, 4, 64, 8, 4096, 14336, &k, &s) != QMM_OK || k != QMM_KERNEL_MFMA_REG || s != 7) return 4;
-    if (qmm_small_m_nt_workspace_bytes(QMM_F16, 4, 64, 6, 4096, 4096) != 8LL * 6 * 4096 * 4) return 5;
+    if (qmm_small_m_nt_workspace_bytes(QMM_F16, 4, 64, 6, 4096, 4096) != 16LL * 6 * 4096 * 4) return 5;
     if (qmm_small_m_batched(QMM_F16, 4, 64, 0, 4, 64, 256, 0, 0, 0, 0, 0, 0) != QMM_OK) return 6;
     printf("%s\n", qmm_kernel_name(QMM_KERNEL_MFMA_REG));
     return 0;
