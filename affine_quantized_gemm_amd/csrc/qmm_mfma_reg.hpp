@@ -449,16 +449,40 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // K are read with coalesced 16-byte loads (whole lines, every lane busy)
             // ahead of the first tile's weights, then staged through its own LDS
             // region and read back in fragment order.  Positions >= K are zero.
+            //
+            // Four wavefronts share a SIMD here and all of them run this
+            // prologue before their weight loads go out, so its vector
+            // instructions are kept few: load j covers rows RPJ j .. RPJ j +
+            // RPJ - 1 (a uniform branch skips loads wholly past row M - 1),
+            // addressed as a uniform base plus a 32-bit lane offset; nothing
+            // is zero-filled that no later step reads.
             constexpr int CPR = KPW * F::KBLK / 8;  // 16-byte chunks per row of the slice
-            constexpr int XG = (16 * CPR + 63) / 64;
-            uint4 xg[XG];
+            static_assert(64 % CPR == 0, "a load instruction covers whole rows of the slice");
+            constexpr int RPJ = 64 / CPR;           // rows per load instruction
+            constexpr int XG = 16 / RPJ;
+            const int lrow = lane / CPR, piece = lane % CPR;
+            u32x4_t xg[XG];
+            if constexpr (VEC) {
+                // (the k-blocks cover K exactly; an element not loaded is
+                // never read, so it starts as whatever its register holds)
+                const uint32_t xoff = static_cast<uint32_t>(
+                    (static_cast<int64_t>(lrow) * K + kb0 * F::KBLK + piece * 8) * 2);
     #pragma unroll
-            for (int j = 0; j < XG; ++j) {
-                const int t = lane + 64 * j;
-                const int row = t / CPR, piece = t % CPR;
+                for (int j = 0; j < XG; ++j) {
+                    xg[j] = __builtin_nondeterministic_value(xg[0]);
+                    if (RPJ * j < M) {
+                        const uint8_t* xb = reinterpret_cast<const uint8_t*>(x) + static_cast<int64_t>(RPJ * j) * K * 2;
+                        if (RPJ * j + lrow < M) xg[j] = *reinterpret_cast<const u32x4_t*>(xb + xoff);
+                    }
+                }
+            } else {
                 const int64_t k = kb0 * F::KBLK + piece * 8;
-                xg[j] = make_uint4(0u, 0u, 0u, 0u);
-                if (row < M && (VEC || k < K)) xg[j] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(row) * K + k);
+    #pragma unroll
+                for (int j = 0; j < XG; ++j) {
+                    const int row = RPJ * j + lrow;
+                    xg[j] = u32x4_t{0u, 0u, 0u, 0u};
+                    if (row < M && k < K) xg[j] = *reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(row) * K + k);
+                }
             }
             load_tile(tile, buf[0], 0, coop_tag);
             __builtin_amdgcn_sched_barrier(0);
@@ -466,17 +490,19 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             uint16_t* xs = reinterpret_cast<uint16_t*>(lds + wave * wave_lds);
     #pragma unroll
             for (int j = 0; j < XG; ++j) {
-                const int t = lane + 64 * j;
-                const int row = t / CPR, piece = t % CPR;
-                if (row < M) *reinterpret_cast<uint4*>(xs + row * XS_ROW + piece * 8) = xg[j];
+                if (RPJ * j < M) {
+                    if (RPJ * j + lrow < M) *reinterpret_cast<u32x4_t*>(xs + (RPJ * j + lrow) * XS_ROW + piece * 8) = xg[j];
+                }
             }
+            // Rows past M - 1 re-read row M - 1: the matrix-core products keep
+            // rows apart, and those output rows are never stored.
+            const int xrow = c < M ? c : M - 1;
     #pragma unroll
             for (int i = 0; i < KPW; ++i)
     #pragma unroll
                 for (int s = 0; s < F::STEPS; ++s) {
                     const int kk = i * F::KBLK + F::src_lane(s, jj) * F::SEG + F::src_slot(s, jj) * 8;
-                    xraw[i][s] = make_uint4(0u, 0u, 0u, 0u);
-                    if (c < M) xraw[i][s] = *reinterpret_cast<const uint4*>(xs + c * XS_ROW + kk);
+                    xraw[i][s] = *reinterpret_cast<const uint4*>(xs + xrow * XS_ROW + kk);
                 }
         }
 
