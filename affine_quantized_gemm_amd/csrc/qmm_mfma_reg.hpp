@@ -207,7 +207,14 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // form).  The row blocks of a column slot or tile have linear workgroup ids
 // congruent mod 8, so they run on one XCD: a tile's weights come from HBM
 // once and from that XCD's L2 for the others (cached loads, not streamed).
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS>
+//
+// Sub-slices (V > 1, single-tile forms only): a wavefront does the work of V
+// wavefronts of the W*V-wavefront form -- V consecutive runs of KPW / V
+// k-blocks, each with its own unit sums, unit product and partial tile --
+// and the partials are combined in the same order, so the results are
+// bit-identical to that form (and to its multi-tile, batched and row-block
+// relatives) with fewer, longer wavefronts.
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS, int V = 1>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K, int64_t ldk,
@@ -217,8 +224,10 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     constexpr bool COOP = MULTI && reg_coop<DT, BITS, GS, KPW, VEC>();
     constexpr int NG = (KPW * F::KBLK + GS - 1) / GS;  // groups touched by one wavefront (vector form)
     constexpr int NGW = NG >= 2 ? NG / 2 : 1;            // 32-bit words holding NG 16-bit values
-    constexpr int NU = KPW * F::PORTIONS;                // units (portions) per wavefront
+    constexpr int NU = KPW * F::PORTIONS / V;            // units (portions) per sub-slice
     static_assert(NU <= 8, "the unit products use the first k-slot quarter only");
+    static_assert(V == 1 || (V == 2 && !MULTI && !SPLIT && KPW % 2 == 0), "sub-slices: single-tile forms");
+    constexpr int KPH = KPW / V;                         // k-blocks per sub-slice
     using Regs = TileRegs<VEC, NGW, KPW, F::SEG_WORDS, F::PORTIONS>;
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int XS_ROW = xs_row_elems(KPW, F::KBLK);
@@ -540,14 +549,15 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         // that puts the largest |X_u|, |O_u| in [2^14, 2^15) before the
         // split; the step's result for row r is then multiplied back by
         // 2^e_r (ufac, exact).  bf16 has fp32's exponent range: no scaling.
-        Frag xo;
-        float ufac[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // fp16: 2^e of output rows 4jj..4jj+3
-        {
+        Frag xo[V];
+        float ufac[V][4];  // fp16: 2^e of output rows 4jj..4jj+3
+    #pragma unroll
+        for (int h = 0; h < V; ++h) {
             const int arow = lane & 15;  // A-operand row this lane supplies
             float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
     #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const int i = u / F::PORTIONS, p = u % F::PORTIONS;
+                const int i = h * KPH + u / F::PORTIONS, p = u % F::PORTIONS;
                 Frag e;
     #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -567,6 +577,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 v8[4 + r] = __shfl(d[r], (lane & 15) + src + 16, 64);
             }
             float vscale = 1.0f;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) ufac[h][r] = 1.0f;
             if constexpr (DT == DT_F16) {
                 // lanes c, c + 32 hold X of row c, lanes c + 16, c + 48 its O
                 float m = 0.0f;
@@ -578,21 +590,21 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 vscale = ldexpf(1.0f, 15 - ex);
                 const float inv = ldexpf(1.0f, ex - 15);
     #pragma unroll
-                for (int r = 0; r < 4; ++r) ufac[r] = __shfl(inv, 4 * jj + r, 64);
+                for (int r = 0; r < 4; ++r) ufac[h][r] = __shfl(inv, 4 * jj + r, 64);
             }
             const bool lo_part = jj >= 2;
     #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 uint32_t h16[2];
     #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int u = e + h;
+                for (int t = 0; t < 2; ++t) {
+                    const int u = e + t;
                     const float v = u < NU ? v8[u] * vscale : 0.0f;
                     const uint32_t hi = DtOps<DT>::rne(v);
                     const uint32_t lo = DtOps<DT>::rne(v - DtOps<DT>::to_f32(static_cast<uint16_t>(hi)));
-                    h16[h] = lo_part ? lo : hi;
+                    h16[t] = lo_part ? lo : hi;
                 }
-                xo.v[e / 2] = h16[0] | (h16[1] << 16);
+                xo[h].v[e / 2] = h16[0] | (h16[1] << 16);
             }
         }
         const UnpackConsts uk = unpack_consts<DT>();
@@ -607,19 +619,20 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 return (want_scale ? r.sb.s[i][p] : r.sb.b[i][p]) & 0xFFFFu;
             }
         };
-        // B operand of the folded unit product: lane (column c, quarter q)
-        // holds b_u (q even) or -s_u (q odd) of units 0..NU-1 (zero beyond NU;
-        // -s is exact: a sign flip).
-        auto unit_frag = [&](const Regs& r) -> Frag {
+        // B operand of the folded unit product of sub-slice h: lane (column c,
+        // quarter q) holds b_u (q even) or -s_u (q odd) of its units
+        // 0..NU-1 (zero beyond NU; -s is exact: a sign flip).
+        auto unit_frag = [&](const Regs& r, int h) -> Frag {
             Frag f;
             const bool odd = (jj & 1) != 0;
     #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int u0 = 2 * v, u1 = u0 + 1;
-                const uint32_t b0 = u0 < NU ? unit_value(r, false, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
-                const uint32_t b1 = u1 < NU ? unit_value(r, false, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
-                const uint32_t s0 = u0 < NU ? unit_value(r, true, u0 / F::PORTIONS, u0 % F::PORTIONS) : 0u;
-                const uint32_t s1 = u1 < NU ? unit_value(r, true, u1 / F::PORTIONS, u1 % F::PORTIONS) : 0u;
+                const int i0 = h * KPH + u0 / F::PORTIONS, i1 = h * KPH + u1 / F::PORTIONS;
+                const uint32_t b0 = u0 < NU ? unit_value(r, false, i0, u0 % F::PORTIONS) : 0u;
+                const uint32_t b1 = u1 < NU ? unit_value(r, false, i1, u1 % F::PORTIONS) : 0u;
+                const uint32_t s0 = u0 < NU ? unit_value(r, true, i0, u0 % F::PORTIONS) : 0u;
+                const uint32_t s1 = u1 < NU ? unit_value(r, true, i1, u1 % F::PORTIONS) : 0u;
                 const uint32_t bias = b0 | (b1 << 16);
                 const uint32_t nscale = (s0 | (s1 << 16)) ^ 0x80008000u;
                 f.v[v] = odd ? nscale : bias;
@@ -634,9 +647,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 // this wavefront's scales and biases of tile t, from the block in LDS
                 r.sb.from_lds(sblk + (parity * 2 * 16 + c) * sb_row + (kb0 * F::KBLK / GS) * 2, 16 * sb_row);
             }
-            float4_t yacc = {0.0f, 0.0f, 0.0f, 0.0f};
+            float4_t yacc[V];
+    #pragma unroll
+            for (int h = 0; h < V; ++h) yacc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     #pragma unroll
             for (int i = 0; i < KPW; ++i) {
+                const int h = i / KPH;
                 Frag bw[F::STEPS];
                 segment_frags<DT, BITS, GS>(r.w[i], bw, uk);
     #pragma unroll
@@ -649,17 +665,20 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                     }
                     const float sc = DtOps<DT>::to_f32(static_cast<uint16_t>(unit_value(r, true, i, p)));
     #pragma unroll
-                    for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(sc, acc[q], yacc[q]);
+                    for (int q = 0; q < 4; ++q) yacc[h][q] = __fmaf_rn(sc, acc[q], yacc[h][q]);
                 }
             }
-            // unit products: + sum_u b_u X_u - sum_u s_u O_u, one step (fp16:
-            // on the scaled sums, then scaled back per row)
-            if constexpr (DT == DT_F16) {
-                const float4_t t = mfma<DT>(xo, unit_frag(r), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+            // unit products: + sum_u b_u X_u - sum_u s_u O_u, one step per
+            // sub-slice (fp16: on the scaled sums, then scaled back per row)
     #pragma unroll
-                for (int q = 0; q < 4; ++q) yacc[q] = __fmaf_rn(ufac[q], t[q], yacc[q]);
-            } else {
-                yacc = mfma<DT>(xo, unit_frag(r), yacc);
+            for (int h = 0; h < V; ++h) {
+                if constexpr (DT == DT_F16) {
+                    const float4_t t = mfma<DT>(xo[h], unit_frag(r, h), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) yacc[h][q] = __fmaf_rn(ufac[h][q], t[q], yacc[h][q]);
+                } else {
+                    yacc[h] = mfma<DT>(xo[h], unit_frag(r, h), yacc[h]);
+                }
             }
             // the next tile's scale/bias block to the other parity; the barrier
             // below publishes it.  That buffer was last read in the previous
@@ -673,11 +692,14 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             // next tile writes the other buffer, and the tile after that can only
             // write this one after passing the next barrier, which the reducing
             // wavefronts reach only after reading.  Cooperative scale/bias blocks
-            // follow the same parity.
+            // follow the same parity.  (Sub-slices, single tile: partial h
+            // in buffer h, read in the order of the wavefronts they stand for.)
             float* rb = reinterpret_cast<float*>(lds + wave * wave_lds) + parity * 4 * PL;
             if (lane < PL) {
     #pragma unroll
-                for (int q = 0; q < 4; ++q) rb[q * PL + lane] = yacc[q];
+                for (int h = 0; h < V; ++h)
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) rb[h * 4 * PL + q * PL + lane] = yacc[h][q];
             }
             if constexpr (DMA) {
                 // (after the partial's stores, so after the compute) this
@@ -693,7 +715,9 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 float v = 0.0f;
     #pragma unroll
                 for (int w = 0; w < W; ++w)
-                    v += reinterpret_cast<const float*>(lds + w * wave_lds)[parity * 4 * PL + q * PL + lane];
+    #pragma unroll
+                    for (int h = 0; h < V; ++h)
+                        v += reinterpret_cast<const float*>(lds + w * wave_lds)[(parity + h) * 4 * PL + q * PL + lane];
                 const int64_t col = col0 + c;
                 const int row = 4 * jj + q;
                 if (col < N && row < M) {
@@ -902,7 +926,7 @@ size_t reg_lds_bytes(int64_t M, int64_t K) {
 // Launch over K range kr of rows a.K long: kr = a.K unsplit, a.K / S split
 // S ways (grid.y = S, each slice with its share of the resident workgroups).
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT = false,
-          bool ROWS = false>
+          bool ROWS = false, int V = 1>
 hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
@@ -943,12 +967,12 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
         // above the default dynamic-LDS limit: raise it once per kernel and device
         static std::atomic<uint64_t> raised{0};
         if (hipError_t e = raise_lds_limit(
-                reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
+                reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V>),
                 raised);
             e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS>),
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(SPLIT ? S : nb),
                             static_cast<unsigned>(RB)),
                        dim3(64 * W), lds, a.stream,
@@ -989,6 +1013,23 @@ inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, i
     return per >= 1 && ntiles > per;
 }
 
+// One tile per workgroup (single-tile forms, alone or on 16-row blocks): 8
+// wavefronts of two sub-slices each instead of 16 wavefronts of kpw
+// k-blocks, bit-identical to them.  A wavefront's per-lane scale/bias
+// gathers touch one line per tile row whatever its share of K, so halving
+// the wavefronts halves those requests.  Measured over every format at
+// N = 1024 / 4096, K = 2048 / 4096, M = 6 / 16: faster for groups of 64 and
+// 128 (up to 0.7 us at 16 rows); groups of 32, with twice the unit sums per
+// sub-slice, lose at 6 rows and keep 16 wavefronts.
+template <int DT, int BITS, int GS, bool ROWS>
+hipError_t launch_single_halved(const MatmulArgs& a, int kpw) {
+    if (kpw == 1) return launch_shape_m<DT, BITS, GS, 8, 2, true, false, false, false, ROWS, 2>(a, a.K);
+    if (kpw == 2) return launch_shape_m<DT, BITS, GS, 8, 4, true, false, false, false, ROWS, 2>(a, a.K);
+    if constexpr (BITS != 4)
+        if (kpw == 4) return launch_shape_m<DT, BITS, GS, 8, 8, true, false, false, false, ROWS, 2>(a, a.K);
+    return hipErrorInvalidValue;
+}
+
 template <int DT, int BITS, int GS>
 hipError_t launch_reg_t(const MatmulArgs& a) {
     RegShape s;
@@ -1010,6 +1051,7 @@ hipError_t launch_reg_t(const MatmulArgs& a) {
             return hipErrorInvalidValue;
         }
         if (!reg_rows1_shape(BITS, GS, a.M, a.N, a.K, s)) return hipErrorInvalidValue;
+        if constexpr (GS >= 64) return launch_single_halved<DT, BITS, GS, true>(a, s.KPW);
         if (s.KPW == 1) return launch_shape_m<DT, BITS, GS, 16, 1, true, false, false, false, true>(a, a.K);
         if (s.KPW == 2) return launch_shape_m<DT, BITS, GS, 16, 2, true, false, false, false, true>(a, a.K);
         if constexpr (BITS != 4)
@@ -1026,6 +1068,10 @@ hipError_t launch_reg_t(const MatmulArgs& a) {
         return hipErrorInvalidValue;
     }
     if (!pick_shape(BITS, GS, a.K, s)) return hipErrorInvalidValue;
+    if constexpr (GS >= 64) {
+        const int64_t nt = (a.N + 15) / 16 * (a.N >= 16 ? a.batch : 1);
+        if (s.W == 16 && s.vec && nt <= reg_grid(nt, 16)) return launch_single_halved<DT, BITS, GS, false>(a, s.KPW);
+    }
     switch (s.W * 100 + s.KPW * 2 + (s.vec ? 1 : 0)) {
         case 402: return launch_shape<DT, BITS, GS, 4, 1, false>(a);
         case 403: return launch_shape<DT, BITS, GS, 4, 1, true>(a);
