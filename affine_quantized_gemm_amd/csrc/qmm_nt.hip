@@ -495,9 +495,9 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
 // 16-byte coalesced loads, and each 16-column tile's B operand comes out of
 // LDS already transposed: no cross-lane shuffles at all.
 //
-// Workgroup: 4 wavefronts own a block of 128 columns (8 tiles, 2 per
+// Workgroup: 8 wavefronts own a block of 256 columns (16 tiles, 2 per
 // wavefront) and one slice of K (blockIdx.y), walked in chunks of 16 KiB of
-// weights (256 rows at 4 bits, 128 at 8) staged in LDS; the next chunk's
+// weights (128 rows at 4 bits, 64 at 8) staged in LDS; the next chunk's
 // weights, activations and scales are loaded into registers while the
 // current one is computed.  A wavefront's tiles are its own for the whole
 // slice, so there is no combine: it stores fp32 partials part[slice][M][N]
@@ -507,22 +507,26 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
 // Rows past the end of the slice inside the last 64-row (32-row) block keep
 // whatever codes the LDS holds but get scale and bias 0 (so w = 0) and zero
 // activations.
-constexpr int NTT_BN = 128;        // columns per workgroup
-constexpr int NTT_THREADS = 256;   // 4 wavefronts, 2 tiles each
+// (256 columns: a 4-bit row piece is a whole 128-byte line, and each row's
+// scale/bias gather serves twice the columns of a 128-column block -- those
+// per-row gathers, one line per row per workgroup, outnumbered the weight
+// requests two to one at 128 columns)
+constexpr int NTT_BN = 256;        // columns per workgroup
+constexpr int NTT_THREADS = 512;   // 8 wavefronts, 2 tiles each
 constexpr int NTT_CHUNK_BYTES = 16384;
 constexpr int NTT_GMAX = NTT_BN / 32;  // groups a block spans at most
 
 template <int BITS>
 struct NttFmt {
-    static constexpr int RP = NTT_BN * BITS / 8;              // bytes of a row piece (64 / 128)
-    static constexpr int KC = NTT_CHUNK_BYTES / RP;           // rows per chunk (256 / 128)
+    static constexpr int RP = NTT_BN * BITS / 8;              // bytes of a row piece (128 / 256)
+    static constexpr int KC = NTT_CHUNK_BYTES / RP;           // rows per chunk (128 / 64)
     static constexpr int BLK = BITS == 4 ? 64 : 32;           // rows per transpose read (16 / 8 per lane group)
     static constexpr int CPR = RP / 16;                       // 16-byte pieces per row
-    static constexpr int WPT = NTT_CHUNK_BYTES / 16 / NTT_THREADS;  // weight pieces per thread (4)
+    static constexpr int WPT = NTT_CHUNK_BYTES / 16 / NTT_THREADS;  // weight pieces per thread (2)
     static constexpr int XS = KC + 8;                         // activation row stride in LDS (elements)
     // LDS position of 16-byte piece c of row r (swizzled so that the
     // transpose reads of 16 consecutive rows spread over the banks)
-    __device__ static constexpr int swz(int r) { return BITS == 4 ? ((r >> 1) & 3) : (r & 7); }
+    __device__ static constexpr int swz(int r) { return r & 7; }
 };
 
 template <int DT, int BITS, int RB, bool PART>
@@ -540,22 +544,10 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, q = lane >> 4;
-    // 4-bit: a 128-byte weight line holds 256 columns, two column blocks.
-    // Workgroups whose linear ids differ by 8 run on one XCD; the two blocks
-    // of a line are given such a pair (when the grid allows), so that the
-    // line comes from HBM once and from that XCD's L2 the second time.
-    int bx = static_cast<int>(blockIdx.x), by = static_cast<int>(blockIdx.y);
-    {
-        const int cb = static_cast<int>(gridDim.x), tot = cb * static_cast<int>(gridDim.y);
-        if (BITS == 4 && cb % 2 == 0 && tot % 16 == 0) {
-            const int L = bx + cb * by;
-            const int P = (L & 7) + 8 * (L >> 4), h = (L >> 3) & 1;
-            bx = 2 * (P % (cb / 2)) + h;
-            by = P / (cb / 2);
-        }
-    }
+    // (a block's row piece is whole 128-byte lines: no two workgroups share one)
+    const int bx = static_cast<int>(blockIdx.x), by = static_cast<int>(blockIdx.y);
     const int64_t n0 = static_cast<int64_t>(bx) * NTT_BN;
-    const int ncols = static_cast<int>(N - n0 < NTT_BN ? N - n0 : NTT_BN);  // 64 or 128
+    const int ncols = static_cast<int>(N - n0 < NTT_BN ? N - n0 : NTT_BN);  // a multiple of 64, <= 256
     const int64_t k_lo = static_cast<int64_t>(by) * kr;
     const int64_t k_hi = k_lo + kr < K ? k_lo + kr : K;
     const int64_t G = N / gs;
@@ -591,11 +583,28 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
         }
         if (tid < KC) {
 #pragma unroll
-            for (int g = 0; g < NTT_GMAX; ++g) {
-                sv[g] = bv[g] = 0;
-                if (g < gw && tid < rows) {
-                    sv[g] = scales[(kc0 + tid) * G + g0 + g];
-                    bv[g] = biases[(kc0 + tid) * G + g0 + g];
+            for (int g = 0; g < NTT_GMAX; ++g) sv[g] = bv[g] = 0;
+            if (tid < rows) {
+                const int64_t o = (kc0 + tid) * G + g0;
+                if (gw == 2 && G % 2 == 0) {
+                    const uint32_t s2 = *reinterpret_cast<const uint32_t*>(scales + o);
+                    const uint32_t b2 = *reinterpret_cast<const uint32_t*>(biases + o);
+                    sv[0] = static_cast<uint16_t>(s2); sv[1] = static_cast<uint16_t>(s2 >> 16);
+                    bv[0] = static_cast<uint16_t>(b2); bv[1] = static_cast<uint16_t>(b2 >> 16);
+                } else if (gw == 4 && G % 4 == 0) {
+                    const uint2 s4 = *reinterpret_cast<const uint2*>(scales + o);
+                    const uint2 b4 = *reinterpret_cast<const uint2*>(biases + o);
+                    sv[0] = static_cast<uint16_t>(s4.x); sv[1] = static_cast<uint16_t>(s4.x >> 16);
+                    sv[2] = static_cast<uint16_t>(s4.y); sv[3] = static_cast<uint16_t>(s4.y >> 16);
+                    bv[0] = static_cast<uint16_t>(b4.x); bv[1] = static_cast<uint16_t>(b4.x >> 16);
+                    bv[2] = static_cast<uint16_t>(b4.y); bv[3] = static_cast<uint16_t>(b4.y >> 16);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < NTT_GMAX; ++g)
+                        if (g < gw) {
+                            sv[g] = scales[o + g];
+                            bv[g] = biases[o + g];
+                        }
                 }
             }
         }
@@ -768,19 +777,29 @@ hipError_t launch_nt_tr(const MatmulArgs& a, int split, int64_t kr) {
 // wide N (>= 128 such workgroups) runs unsplit.
 NtPlan nt_plan(int bits, int64_t M, int64_t N, int64_t K) {
     (void)M;
-    const int64_t groups = (N + 127) / 128;  // 128-column workgroups
+    const int64_t groups = (N + 127) / 128;  // 128-column workgroups of the 16-wavefront form
     if (bits != 6 && groups >= 32) {
-        // transpose-read form: about 512 workgroups (two per CU), slices of
-        // whole 32-row steps, at most 16 (the partial sums grow with the
-        // slices; with fewer than 32 column blocks, e.g. N = 1024, the
-        // 16-wavefront form below fills the chip with fewer slices)
-        if (groups >= 256) return NtPlan{true, 1, K, true};
-        int64_t split = (512 + groups / 2) / groups;
-        if (split > 16) split = 16;
-        if (split > K / 32) split = K / 32;
-        if (split < 2) return NtPlan{true, 1, K, true};
-        const int64_t ks = ((K + split - 1) / split + 31) / 32 * 32;
-        return NtPlan{true, static_cast<int>((K + ks - 1) / ks), ks, true};
+        // transpose-read form (256-column workgroups): slices of whole
+        // 16 KiB chunks (128 rows at 4 bits, 64 at 8) that divide K, with
+        // 256..512 workgroups -- one or two per CU; otherwise whole chunks
+        // and at least 256 workgroups.  Measured at M = 6: 4096 x 4096 on
+        // 16 slices of 256 rows 13.0 us (8 / 12 / 24 / 32 slices: 17.5 /
+        // 14.8 / 14.9 / 14.1); gate/up (56 blocks) on 8 slices 26.4 us (4 /
+        // 5 / 6 / 7 / 10 / 12 / 16: 30.3 / 31.4 / 29.8 / 28.2 / 32.7 / 31.5 /
+        // 31.1); down (K = 14336) on 16 slices of 896 rows 30.8 us (14 / 20
+        // / 24 / 32: 33.0 / 34.5 / 32.4 / 31.2).
+        const int64_t blocks = (N + 255) / 256;
+        const int64_t kc = bits == 4 ? 128 : 64;
+        if (blocks >= 256 || K < 2 * kc) return NtPlan{true, 1, K, true};
+        for (int64_t s = 2; s <= 32; ++s)
+            if (K % s == 0 && (K / s) % kc == 0 && blocks * s >= 256 && blocks * s <= 512)
+                return NtPlan{true, static_cast<int>(s), K / s, true};
+        for (int64_t s = 2; s <= 32; ++s) {
+            const int64_t ks = ((K + s - 1) / s + kc - 1) / kc * kc;
+            const int64_t se = (K + ks - 1) / ks;
+            if (blocks * se >= 256 || s == 32 || ks == kc)
+                return se < 2 ? NtPlan{true, 1, K, true} : NtPlan{true, static_cast<int>(se), ks, true};
+        }
     }
     NtPlan p{false, 1, K, false};
     if (groups >= 128) return NtPlan{true, 1, K, false};  // wide N: enough workgroups unsplit

@@ -352,23 +352,26 @@ def test_nt_validation():
 
 
 def test_nt_split_plan_and_validation():
-    """qmm_small_m_nt_ws: 128-column workgroups with K slices.  4/8-bit with
-    at least 32 column blocks (the transpose-read form): about 512
-    workgroups, at most 16 slices, unsplit from 256 blocks; otherwise (6-bit,
-    or N below 4096) the 16-wavefront form: about 256 workgroups, at most 16
-    slices, unsplit from 128 blocks; unsplit when K is short; errors before
-    any HIP call."""
+    """qmm_small_m_nt_ws: column blocks with K slices.  4/8-bit with N >=
+    4096 (the transpose-read form, 256-column blocks): slices of whole 16 KiB
+    chunks (128 rows at 4 bits, 64 at 8) dividing K for 256..512 workgroups,
+    else whole chunks for at least 256, unsplit from 256 blocks; otherwise
+    (6-bit, or N below 4096) the 16-wavefront form with 128-column blocks:
+    about 256 workgroups, at most 16 slices, unsplit from 128 blocks;
+    unsplit when K is short; errors before any HIP call."""
     f16, bf16 = Q.QMM_F16, Q.QMM_BF16
     wb = Q.qmm_small_m_nt_workspace_bytes
-    assert wb(f16, 4, 64, 6, 4096, 4096) == 16 * 6 * 4096 * 4      # 32 blocks x 16 slices (transpose reads)
+    assert wb(f16, 4, 64, 6, 4096, 4096) == 16 * 6 * 4096 * 4      # 16 blocks x 16 slices of 256 rows (transpose reads)
     assert wb(bf16, 8, 32, 6, 4096, 4096) == 16 * 6 * 4096 * 4
     assert wb(f16, 6, 64, 6, 4096, 4096) == 8 * 6 * 4096 * 4       # 6-bit: 32 x 8 slices
     assert wb(f16, 4, 64, 6, 1024, 4096) == 16 * 6 * 1024 * 4      # 8 blocks: the 16-wavefront form, 16 slices
-    assert wb(f16, 4, 64, 4, 4096, 14336) == 16 * 4 * 4096 * 4
-    assert wb(f16, 4, 64, 6, 14336, 4096) == 5 * 6 * 14336 * 4     # 112 blocks x 5 slices
+    assert wb(f16, 4, 64, 4, 4096, 14336) == 16 * 4 * 4096 * 4     # 16 x 16 slices of 896 rows (7 chunks)
+    assert wb(f16, 4, 64, 6, 14336, 4096) == 8 * 6 * 14336 * 4     # 56 blocks x 8 slices of 512 rows
+    assert wb(bf16, 8, 64, 6, 4096, 4160) == 17 * 6 * 4096 * 4     # no divisor fits: 16 x 17 slices of 256 rows (the last 64)
+    assert wb(f16, 4, 64, 6, 32768, 4096) == 2 * 6 * 32768 * 4     # 128 blocks x 2 slices
     assert wb(f16, 4, 64, 64, 1024, 4160) == 15 * 64 * 1024 * 4    # slices of 288 rows, the last shorter
     assert wb(f16, 6, 64, 6, 16384, 4096) == 0                     # 6-bit, 128 blocks: unsplit
-    assert wb(f16, 4, 64, 6, 32768, 4096) == 0                     # 256 blocks: unsplit
+    assert wb(f16, 4, 64, 6, 65536, 4096) == 0                     # 256 blocks: unsplit
     assert wb(f16, 4, 64, 6, 256, 96) == 0                         # one slice of K
     assert wb(f16, 4, 64, -1, 256, 96) == Q.QMM_ERR_INVALID_ARG
     assert wb(f16, 4, 64, 6, 96, 96) == Q.QMM_ERR_UNSUPPORTED
