@@ -529,7 +529,7 @@ struct NttFmt {
     __device__ static constexpr int swz(int r) { return r & 7; }
 };
 
-template <int DT, int BITS, int RB, bool PART>
+template <int DT, int BITS, int RB, bool PART, int SBW>
 __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ part, int M, int64_t N,
@@ -552,78 +552,118 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
     const int64_t k_hi = k_lo + kr < K ? k_lo + kr : K;
     const int64_t G = N / gs;
     const int64_t g0 = n0 / gs;
-    const int gw = (ncols + gs - 1) / gs;  // groups of this block (1..4)
+    const int gw = (ncols + gs - 1) / gs;  // groups of this block (1..8)
+    // SBW > 0: every block spans SBW groups (N a multiple of the block
+    // width), and a row's SBW scales load as one 4-, 8- or 16-byte run
+    static_assert(SBW == 0 || SBW == 2 || SBW == 4 || SBW == 8, "scale run of 2, 4 or 8 values");
+    constexpr bool vec_sb = SBW > 0;
     const int64_t row_bytes = N * BITS / 8;
     const uint8_t* const wbase = reinterpret_cast<const uint8_t*>(wq) + n0 * BITS / 8;
 
     // activation rows M .. 16 RB - 1 stay zero for the whole kernel
     for (int i = tid; i < (16 * RB - M) * XS; i += NTT_THREADS) x_lds[M * XS + i] = 0;
 
-    // register prefetch of one chunk
-    uint4 wv[F::WPT];
+    // register prefetch, two chunks deep: a chunk's weights, activations
+    // and scales in one buffer
     constexpr int XPT = (16 * RB * KC / 8 + NTT_THREADS - 1) / NTT_THREADS;  // activation pieces per thread
-    uint4 xv[XPT];
-    uint16_t sv[NTT_GMAX], bv[NTT_GMAX];
-    auto load_chunk = [&](int64_t kc0) __attribute__((always_inline)) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // (a native vector: stays in registers)
+    struct ChunkRegs {
+        v4u wv[F::WPT];
+        v4u xv[XPT];
+        uint32_t sv[NTT_GMAX], bv[NTT_GMAX];  // packed pairs (vec_sb) or one value each
+    };
+    ChunkRegs cr0, cr1;
+    auto load_chunk = [&](int64_t kc0, ChunkRegs& cb) __attribute__((always_inline)) {
+        auto& wv = cb.wv;
+        auto& xv = cb.xv;
+        auto& sv = cb.sv;
+        auto& bv = cb.bv;
+        // Every lane issues every load, from a clamped address where its
+        // piece lies past the slice, past M or past the block (the counter
+        // then counts the same loads on every path, so each wait is exact;
+        // a load skipped on some path makes every later wait drain the
+        // queue).  What such a load brings is never used: rows past the
+        // slice get scale and bias 0 and meet activations read from valid
+        // rows, activation rows past M and columns past the block are never
+        // staged or computed.  A chunk past the slice (the prefetch of the
+        // last steps) is never staged: its loads all read the first 16
+        // bytes of each array (one line).
+        const bool past = kc0 >= k_hi;
+        if (past) kc0 = k_lo;
         const int rows = static_cast<int>(k_hi - kc0 < KC ? k_hi - kc0 : KC);
 #pragma unroll
         for (int i = 0; i < F::WPT; ++i) {
             const int p = tid + NTT_THREADS * i;
             const int r = p / F::CPR, c = (p % F::CPR) ^ F::swz(r);
-            if (r < rows && c * 16 * 8 / BITS < ncols)
-                wv[i] = *reinterpret_cast<const uint4*>(wbase + (kc0 + r) * row_bytes + c * 16);
+            const int rr = r < rows ? r : rows - 1;
+            const int cc = c * 16 * 8 / BITS < ncols ? c : 0;
+            const int64_t wo = past ? 0 : (kc0 + rr) * row_bytes + cc * 16;
+            wv[i] = *reinterpret_cast<const v4u*>(wbase + wo);
         }
         const int cpr = KC / 8;  // activation pieces per row
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int p = tid + NTT_THREADS * i;
             const int m = p / cpr, c = p % cpr;
-            xv[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M && 8 * c < rows) xv[i] = *reinterpret_cast<const uint4*>(x + m * K + kc0 + 8 * c);
+            const int mm = m < M ? m : M - 1;
+            const int ccx = 8 * c < rows ? c : 0;
+            const int64_t xo = past ? 0 : static_cast<int64_t>(mm) * K + kc0 + 8 * ccx;
+            xv[i] = *reinterpret_cast<const v4u*>(x + xo);
         }
-        if (tid < KC) {
+        {
+            // this row's run of gw scales (biases): one load where it is an
+            // aligned run of 2, 4 or 8 (a separate kernel), kept packed until
+            // staged; nothing is written to these registers but the loads
+            // (a later write to a register a load targets waits for every
+            // load before it).  Lanes past KC load the first line of the
+            // arrays (never staged); rows past the slice are staged as 0.
+            const int r = tid < rows ? tid : rows - 1;
+            const int64_t o = past || tid >= KC ? 0 : (kc0 + r) * G + g0;
+            if constexpr (SBW == 2) {
+                sv[0] = *reinterpret_cast<const uint32_t*>(scales + o);
+                bv[0] = *reinterpret_cast<const uint32_t*>(biases + o);
+            } else if constexpr (SBW == 4) {
+                const uint2 s4 = *reinterpret_cast<const uint2*>(scales + o);
+                const uint2 b4 = *reinterpret_cast<const uint2*>(biases + o);
+                sv[0] = s4.x; sv[1] = s4.y; bv[0] = b4.x; bv[1] = b4.y;
+            } else if constexpr (SBW == 8) {
+                const uint4 s8 = *reinterpret_cast<const uint4*>(scales + o);
+                const uint4 b8 = *reinterpret_cast<const uint4*>(biases + o);
+                sv[0] = s8.x; sv[1] = s8.y; sv[2] = s8.z; sv[3] = s8.w;
+                bv[0] = b8.x; bv[1] = b8.y; bv[2] = b8.z; bv[3] = b8.w;
+            } else {
 #pragma unroll
-            for (int g = 0; g < NTT_GMAX; ++g) sv[g] = bv[g] = 0;
-            if (tid < rows) {
-                const int64_t o = (kc0 + tid) * G + g0;
-                if (gw == 2 && G % 2 == 0) {
-                    const uint32_t s2 = *reinterpret_cast<const uint32_t*>(scales + o);
-                    const uint32_t b2 = *reinterpret_cast<const uint32_t*>(biases + o);
-                    sv[0] = static_cast<uint16_t>(s2); sv[1] = static_cast<uint16_t>(s2 >> 16);
-                    bv[0] = static_cast<uint16_t>(b2); bv[1] = static_cast<uint16_t>(b2 >> 16);
-                } else if (gw == 4 && G % 4 == 0) {
-                    const uint2 s4 = *reinterpret_cast<const uint2*>(scales + o);
-                    const uint2 b4 = *reinterpret_cast<const uint2*>(biases + o);
-                    sv[0] = static_cast<uint16_t>(s4.x); sv[1] = static_cast<uint16_t>(s4.x >> 16);
-                    sv[2] = static_cast<uint16_t>(s4.y); sv[3] = static_cast<uint16_t>(s4.y >> 16);
-                    bv[0] = static_cast<uint16_t>(b4.x); bv[1] = static_cast<uint16_t>(b4.x >> 16);
-                    bv[2] = static_cast<uint16_t>(b4.y); bv[3] = static_cast<uint16_t>(b4.y >> 16);
-                } else {
-#pragma unroll
-                    for (int g = 0; g < NTT_GMAX; ++g)
-                        if (g < gw) {
-                            sv[g] = scales[o + g];
-                            bv[g] = biases[o + g];
-                        }
+                for (int g = 0; g < NTT_GMAX; ++g) {
+                    const int gg = g < gw ? g : gw - 1;
+                    sv[g] = scales[o + gg];
+                    bv[g] = biases[o + gg];
                 }
             }
         }
     };
-    auto stage_chunk = [&]() __attribute__((always_inline)) {
+    auto stage_chunk = [&](int64_t kc0, const ChunkRegs& cb) __attribute__((always_inline)) {
+        const int srows = static_cast<int>(k_hi - kc0 < KC ? k_hi - kc0 : KC);
+        const auto& wv = cb.wv;
+        const auto& xv = cb.xv;
+        const auto& sv = cb.sv;
+        const auto& bv = cb.bv;
 #pragma unroll
-        for (int i = 0; i < F::WPT; ++i) *reinterpret_cast<uint4*>(w_lds + 16 * (tid + NTT_THREADS * i)) = wv[i];
+        for (int i = 0; i < F::WPT; ++i) *reinterpret_cast<v4u*>(w_lds + 16 * (tid + NTT_THREADS * i)) = wv[i];
         const int cpr = KC / 8;
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int p = tid + NTT_THREADS * i;
             const int m = p / cpr, c = p % cpr;
-            if (m < M) *reinterpret_cast<uint4*>(x_lds + m * XS + 8 * c) = xv[i];
+            if (m < M) *reinterpret_cast<v4u*>(x_lds + m * XS + 8 * c) = xv[i];
         }
         if (tid < KC) {
+            // (groups past gw stage whatever the registers hold: never read)
 #pragma unroll
             for (int g = 0; g < NTT_GMAX; ++g) {
-                s_lds[g * KC + tid] = sv[g];
-                b_lds[g * KC + tid] = bv[g];
+                const uint32_t sg = vec_sb ? sv[g >> 1] >> (16 * (g & 1)) : sv[g];
+                const uint32_t bg = vec_sb ? bv[g >> 1] >> (16 * (g & 1)) : bv[g];
+                s_lds[g * KC + tid] = static_cast<uint16_t>(tid < srows ? sg : 0u);
+                b_lds[g * KC + tid] = static_cast<uint16_t>(tid < srows ? bg : 0u);
             }
         }
     };
@@ -637,11 +677,7 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
     const bool live = 16 * t0 < ncols;            // (uniform: a 64-column block has tiles 0..3)
     const int gt = 16 * t0 / gs;                  // the two tiles' group (gs >= 32)
 
-    load_chunk(k_lo);
-    for (int64_t kc0 = k_lo; kc0 < k_hi; kc0 += KC) {
-        stage_chunk();
-        __syncthreads();
-        if (kc0 + KC < k_hi) load_chunk(kc0 + KC);  // in flight during the compute below
+    auto compute_chunk = [&](int64_t kc0) __attribute__((always_inline)) {
         const int rows = static_cast<int>(k_hi - kc0 < KC ? k_hi - kc0 : KC);
         if (live) {
             for (int blk = 0; blk < rows; blk += BLK) {
@@ -703,7 +739,24 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
                 }
             }
         }
+    };
+    // chunk c is staged from buffer c % 2, whose next load (chunk c + 2) is
+    // then in flight during the compute of chunks c and c + 1
+    // (every step issues its prefetch, past the slice too: the same loads
+    // on every path keep the compiler's waits to "this buffer's loads")
+    auto step = [&](int64_t kc0, ChunkRegs& cb) __attribute__((always_inline)) {
+        const bool in = kc0 < k_hi;
+        if (in) stage_chunk(kc0, cb);
+        __syncthreads();
+        load_chunk(kc0 + 2 * KC, cb);
+        if (in) compute_chunk(kc0);
         __syncthreads();  // the chunk's LDS is overwritten next
+    };
+    load_chunk(k_lo, cr0);
+    load_chunk(k_lo + KC, cr1);
+    for (int64_t kc0 = k_lo; kc0 < k_hi; kc0 += 2 * KC) {
+        step(kc0, cr0);
+        step(kc0 + KC, cr1);
     }
 
     if (!live) return;
@@ -729,16 +782,16 @@ constexpr size_t ntt_lds_bytes() {
     return NTT_CHUNK_BYTES + 2 * (16 * RB * NttFmt<BITS>::XS + 2 * NTT_GMAX * NttFmt<BITS>::KC);
 }
 
-template <int DT, int BITS, int RB, bool PART>
-hipError_t launch_nt_tr_t(const MatmulArgs& a, int split, int64_t kr) {
+template <int DT, int BITS, int RB, bool PART, int SBW>
+hipError_t launch_nt_tr_s(const MatmulArgs& a, int split, int64_t kr) {
     constexpr size_t lds = ntt_lds_bytes<BITS, RB>();
     if (lds > 65536) {
         static std::atomic<uint64_t> raised{0};
-        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&nt_tr_kernel<DT, BITS, RB, PART>), raised);
+        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&nt_tr_kernel<DT, BITS, RB, PART, SBW>), raised);
             e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((nt_tr_kernel<DT, BITS, RB, PART>),
+    hipLaunchKernelGGL((nt_tr_kernel<DT, BITS, RB, PART, SBW>),
                        dim3(static_cast<unsigned>((a.N + NTT_BN - 1) / NTT_BN), static_cast<unsigned>(split)),
                        dim3(NTT_THREADS), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
                        static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
@@ -746,6 +799,18 @@ hipError_t launch_nt_tr_t(const MatmulArgs& a, int split, int64_t kr) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if constexpr (PART) return launch_reduce_partials(DT, a.part, a.y, split, a.M * a.N, a.stream);
     return hipSuccess;
+}
+
+// the scale-run width: every block whole (N a multiple of 256) and 2, 4 or 8
+// groups per block, else values one by one
+template <int DT, int BITS, int RB, bool PART>
+hipError_t launch_nt_tr_t(const MatmulArgs& a, int split, int64_t kr) {
+    if (a.N % NTT_BN == 0) {
+        if (a.gs == NTT_BN / 2) return launch_nt_tr_s<DT, BITS, RB, PART, 2>(a, split, kr);
+        if (a.gs == NTT_BN / 4) return launch_nt_tr_s<DT, BITS, RB, PART, 4>(a, split, kr);
+        if (a.gs == NTT_BN / 8) return launch_nt_tr_s<DT, BITS, RB, PART, 8>(a, split, kr);
+    }
+    return launch_nt_tr_s<DT, BITS, RB, PART, 0>(a, split, kr);
 }
 
 template <int DT, int BITS>
