@@ -844,25 +844,25 @@ NtPlan nt_plan(int bits, int64_t M, int64_t N, int64_t K) {
     (void)M;
     const int64_t groups = (N + 127) / 128;  // 128-column workgroups of the 16-wavefront form
     if (bits != 6 && groups >= 32) {
-        // transpose-read form (256-column workgroups): slices of whole
-        // 16 KiB chunks (128 rows at 4 bits, 64 at 8) that divide K, with
-        // 256..512 workgroups -- one or two per CU; otherwise whole chunks
-        // and at least 256 workgroups.  Measured at M = 6: 4096 x 4096 on
-        // 16 slices of 256 rows 13.0 us (8 / 12 / 24 / 32 slices: 17.5 /
-        // 14.8 / 14.9 / 14.1); gate/up (56 blocks) on 8 slices 26.4 us (4 /
-        // 5 / 6 / 7 / 10 / 12 / 16: 30.3 / 31.4 / 29.8 / 28.2 / 32.7 / 31.5 /
-        // 31.1); down (K = 14336) on 16 slices of 896 rows 30.8 us (14 / 20
-        // / 24 / 32: 33.0 / 34.5 / 32.4 / 31.2).
+        // transpose-read form (256-column workgroups): the fewest slices of
+        // whole 16 KiB chunks (128 rows at 4 bits, 64 at 8) that divide K and
+        // give at least 224 workgroups (7/8 of the CUs: longer slices keep
+        // more chunks in the prefetch pipeline), at most 512; otherwise
+        // whole chunks and at least 224.  Measured at M = 6: 4096 x 4096 on
+        // 16 slices of 256 rows 11.0 us (8 / 32 slices: 12.3 / 13.3);
+        // gate/up (56 blocks) on 4 slices 19.8 us (8 / 16 / 32: 22.0 / 24.9
+        // / 34.1); down (K = 14336) on 14 slices of 1024 rows 22.4 us (8 /
+        // 16 / 28: 28.6 / 22.0 / 25.8).
         const int64_t blocks = (N + 255) / 256;
         const int64_t kc = bits == 4 ? 128 : 64;
         if (blocks >= 256 || K < 2 * kc) return NtPlan{true, 1, K, true};
         for (int64_t s = 2; s <= 32; ++s)
-            if (K % s == 0 && (K / s) % kc == 0 && blocks * s >= 256 && blocks * s <= 512)
+            if (K % s == 0 && (K / s) % kc == 0 && blocks * s >= 224 && blocks * s <= 512)
                 return NtPlan{true, static_cast<int>(s), K / s, true};
         for (int64_t s = 2; s <= 32; ++s) {
             const int64_t ks = ((K + s - 1) / s + kc - 1) / kc * kc;
             const int64_t se = (K + ks - 1) / ks;
-            if (blocks * se >= 256 || s == 32 || ks == kc)
+            if (blocks * se >= 224 || s == 32 || ks == kc)
                 return se < 2 ? NtPlan{true, 1, K, true} : NtPlan{true, static_cast<int>(se), ks, true};
         }
     }

@@ -158,10 +158,10 @@ int qmm_small_m_nt(int dt, int bits, int group_size, int64_t M, int64_t N, int64
  * with column-block workgroups each taking one slice of K and leaving fp32
  * partial outputs ([split][M][N]) in a caller-provided workspace; a second
  * kernel adds them in slice order and rounds once (deterministic).  4/8-bit
- * codes with N >= 4096: 256-column blocks on slices of whole 16 KiB chunks
- * dividing K, for 256..512 workgroups (at most 32 slices; unsplit from 256
- * blocks); otherwise 128-column blocks on at most 16 slices for about 256
- * workgroups.
+ * codes with N >= 4096: 256-column blocks on the fewest slices of whole
+ * 16 KiB chunks dividing K that give 224..512 workgroups (at most 32 slices;
+ * unsplit from 256 blocks); otherwise 128-column blocks on at most 16 slices
+ * for about 256 workgroups.
  * Where the plan does not split (wide N, short K) the workspace may be NULL
  * and the call is exactly qmm_small_m_nt.
  * qmm_small_m_nt_workspace_bytes: bytes of workspace the call needs (0: no

@@ -353,9 +353,10 @@ def test_nt_validation():
 
 def test_nt_split_plan_and_validation():
     """qmm_small_m_nt_ws: column blocks with K slices.  4/8-bit with N >=
-    4096 (the transpose-read form, 256-column blocks): slices of whole 16 KiB
-    chunks (128 rows at 4 bits, 64 at 8) dividing K for 256..512 workgroups,
-    else whole chunks for at least 256, unsplit from 256 blocks; otherwise
+    4096 (the transpose-read form, 256-column blocks): the fewest slices of
+    whole 16 KiB chunks (128 rows at 4 bits, 64 at 8) dividing K for
+    224..512 workgroups, else whole chunks for at least 224, unsplit from 256
+    blocks; otherwise
     (6-bit, or N below 4096) the 16-wavefront form with 128-column blocks:
     about 256 workgroups, at most 16 slices, unsplit from 128 blocks;
     unsplit when K is short; errors before any HIP call."""
@@ -365,8 +366,8 @@ def test_nt_split_plan_and_validation():
     assert wb(bf16, 8, 32, 6, 4096, 4096) == 16 * 6 * 4096 * 4
     assert wb(f16, 6, 64, 6, 4096, 4096) == 8 * 6 * 4096 * 4       # 6-bit: 32 x 8 slices
     assert wb(f16, 4, 64, 6, 1024, 4096) == 16 * 6 * 1024 * 4      # 8 blocks: the 16-wavefront form, 16 slices
-    assert wb(f16, 4, 64, 4, 4096, 14336) == 16 * 4 * 4096 * 4     # 16 x 16 slices of 896 rows (7 chunks)
-    assert wb(f16, 4, 64, 6, 14336, 4096) == 8 * 6 * 14336 * 4     # 56 blocks x 8 slices of 512 rows
+    assert wb(f16, 4, 64, 4, 4096, 14336) == 14 * 4 * 4096 * 4     # 16 x 14 slices of 1024 rows (8 chunks)
+    assert wb(f16, 4, 64, 6, 14336, 4096) == 4 * 6 * 14336 * 4     # 56 blocks x 4 slices of 1024 rows
     assert wb(bf16, 8, 64, 6, 4096, 4160) == 17 * 6 * 4096 * 4     # no divisor fits: 16 x 17 slices of 256 rows (the last 64)
     assert wb(f16, 4, 64, 6, 32768, 4096) == 2 * 6 * 32768 * 4     # 128 blocks x 2 slices
     assert wb(f16, 4, 64, 64, 1024, 4160) == 15 * 64 * 1024 * 4    # slices of 288 rows, the last shorter
