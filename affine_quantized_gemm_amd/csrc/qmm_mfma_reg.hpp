@@ -366,11 +366,14 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     // `blk`), then its weight slice (slot `slot`)
     auto dma_col0 = [&](int tile) -> int { return tile < nfull ? tile * 16 : lastc; };
     // Past the workgroup's last tile the ring still issues its loads (the
-    // waits count them), from the first KiB of this K range of the weights
-    // instead: L2-resident after the first such load, and inside the array
-    // (these forms run only where N spans many 16-row tiles, and a tile's
-    // 16 rows hold at least 1 KiB).  Those slots are never read.
+    // waits count them), from the first KiB of the workgroup's first tile
+    // instead: inside the array (these forms run only where N spans many
+    // 16-row tiles, and a tile's 16 rows hold at least 1 KiB) and a
+    // different line per workgroup -- one KiB shared by every workgroup made
+    // a hot spot of their last iterations.  Those slots are never read.
     const uint32_t dummy_off = static_cast<uint32_t>(lane) * 16;
+    const uint8_t* const dummy_src =
+        reinterpret_cast<const uint8_t*>(wq) + static_cast<int64_t>(dma_col0(static_cast<int>(blockIdx.x))) * row_bytes;
     // (two branches on a uniform condition, not selects: a select between
     // the offsets makes the compiler index a stack copy of dma_off)
     auto dma_tile = [&](int tile, int slot, int blk) __attribute__((always_inline)) {
@@ -383,9 +386,9 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
 #pragma unroll
             for (int i = 0; i < NI; ++i) dma16<!ROWS>(wt, dma_off[i], m0w + 1024 * i);
         } else {
-            if (sc_on) dma16(wq, dummy_off, m0s);
+            if (sc_on) dma16(dummy_src, dummy_off, m0s);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) dma16(wq, dummy_off, m0w + 1024 * i);
+            for (int i = 0; i < NI; ++i) dma16(dummy_src, dummy_off, m0w + 1024 * i);
         }
     };
     auto load_tile = [&](int64_t tile, Regs& r, int slot, auto coop_tag) __attribute__((always_inline)) {

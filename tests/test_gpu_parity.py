@@ -419,7 +419,7 @@ def test_nt_shapes(Q, dt, bits, gs, M, N, K):
 
 
 @pytest.mark.parametrize("dt,bits,gs,M,N,K", [
-    ("f16", 4, 64, 6, 4096, 4096),      # 32 workgroups of 128 columns x 8 slices
+    ("f16", 4, 64, 6, 4096, 4096),      # transpose reads: 16 blocks of 256 columns x 16 slices
     ("bf16", 6, 128, 36, 384, 640),     # 3 workgroups x 10 slices of 64 rows
     ("f16", 8, 32, 16, 64, 8192),       # one workgroup holding 64 columns, 16 slices
     ("bf16", 4, 32, 64, 1024, 4160),    # 15 slices, the last one shorter
@@ -446,6 +446,58 @@ def test_nt_split(Q, dt, bits, gs, M, N, K):
     y3 = Q.small_m_nt(xc, wq, sc, bi, bits, gs)
     ok3, worst3 = O.within_tolerance(O.to_f64(synth.to_oracle(y3), dt), yo, T)
     assert ok3, worst3
+
+
+@pytest.mark.parametrize("dt,bits,gs,M,N,K", [
+    ("bf16", 8, 32, 3, 4096, 4160),     # 8 groups per block; no divisor fits: 17 slices, the last 64 rows
+    ("f16", 8, 128, 16, 4096, 4096),    # 2 groups per block, one full row block
+    ("f16", 4, 64, 1, 4160, 2048),      # 17 blocks, the last 64 columns wide (scales one by one)
+    ("bf16", 4, 64, 40, 4096, 4096),    # 3 row blocks
+    ("f16", 4, 32, 64, 4352, 1024),     # 4 row blocks, 17 blocks
+])
+def test_nt_transpose_read_split(Q, dt, bits, gs, M, N, K):
+    """The transpose-read K split (4/8-bit codes, N >= 4096): scale runs of
+    8, 2 and 1 values, a 64-column last block, a short last slice, 1..4 row
+    blocks.  Every output against the oracle; a second call on the same
+    workspace bit-identical."""
+    need = Q.nt_workspace_bytes(DT[dt], bits, gs, M, N, K)
+    print(f"nt transpose-read split {dt} {bits}-bit gs{gs} M={M} N={N} K={K} workspace={need}", flush=True)
+    assert need > 0  # a split
+    w = synth.normal((K, N), 0.02, dt, 9950 + M, outlier_frac=0.01)
+    owq, osc, obi = oracle_quant(w, dt, bits, gs)
+    x = synth.normal((M, K), 1.0, dt, 9951 + M)
+    wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+    xc = x.cuda()
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    y = Q.small_m_nt(xc, wq, sc, bi, bits, gs, split=True, workspace=ws)
+    torch.cuda.synchronize()
+    yo, T = O.qmm_nt(synth.to_oracle(x), owq, osc, obi, dt, bits, gs, N)
+    ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+    assert ok, worst
+    y2 = Q.small_m_nt(xc, wq, sc, bi, bits, gs, split=True, workspace=ws)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_nt_split_workspace_reuse(Q):
+    """One workspace serves a sequence of K-split calls of different shapes
+    and forms (transpose reads on 1..2 row blocks, the 16-wavefront form):
+    every result bit-identical to a call on a fresh workspace."""
+    cases = [("f16", 4, 64, 6, 4096, 4096), ("f16", 4, 64, 16, 14336, 4096), ("bf16", 8, 64, 24, 4096, 2048),
+             ("f16", 6, 64, 6, 1024, 4096), ("bf16", 4, 32, 2, 8192, 1024)]
+    need = max(Q.nt_workspace_bytes(DT[c[0]], *c[1:]) for c in cases)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    prepared = []
+    for i, (dt, bits, gs, M, N, K) in enumerate(cases):
+        w = synth.normal((K, N), 0.02, dt, 9980 + i, device="cuda")
+        wq, sc, bi = Q.quantize(w, bits, gs)
+        prepared.append((synth.normal((M, K), 1.0, dt, 9990 + i, device="cuda"), wq, sc, bi, bits, gs))
+    for rep in range(2):
+        for (dt, bits, gs, M, N, K), (x, wq, sc, bi, b, g) in zip(cases, prepared):
+            print(f"nt workspace reuse pass {rep}: {dt} {bits}-bit gs{gs} M={M} N={N} K={K}", flush=True)
+            y_fresh = Q.small_m_nt(x, wq, sc, bi, b, g, split=True)
+            y = Q.small_m_nt(x, wq, sc, bi, b, g, split=True, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y_fresh.view(torch.int16)), (dt, bits, gs, M, N, K)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
