@@ -9,10 +9,10 @@ namespace {
 
 // y = the split partial outputs added in split order (deterministic), then
 // rounded once to dt.  part is [S][M*N] fp32.  A thread takes 4 consecutive
-// outputs (16-byte loads) and keeps 8 slices' loads in flight before adding
+// outputs (16-byte loads) and keeps 16 slices' loads in flight before adding
 // them in order: one slice at a time, each add waited for its load, made a
-// 16-way split a chain of 16 round trips.  One wavefront per workgroup, so
-// that a few thousand outputs still spread over many CUs.
+// 16-way split a chain of 16 round trips (8 in flight: two).  One wavefront
+// per workgroup, so that a few thousand outputs still spread over many CUs.
 template <int DT>
 __global__ __launch_bounds__(64) void reduce_partials_kernel(const float* __restrict__ part,
                                                              uint16_t* __restrict__ y, int S, int64_t mn) {
@@ -21,13 +21,13 @@ __global__ __launch_bounds__(64) void reduce_partials_kernel(const float* __rest
     if (i >= mn) return;
     if (i + 4 <= mn && mn % 4 == 0) {
         f4_t v = *reinterpret_cast<const f4_t*>(part + i);
-        for (int s = 1; s < S; s += 8) {
-            f4_t t[8];
+        for (int s = 1; s < S; s += 16) {
+            f4_t t[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 16; ++j)
                 if (s + j < S) t[j] = *reinterpret_cast<const f4_t*>(part + static_cast<int64_t>(s + j) * mn + i);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 16; ++j)
                 if (s + j < S) v += t[j];
         }
         uint32_t lo = DtOps<DT>::rne(v[0]) | (static_cast<uint32_t>(DtOps<DT>::rne(v[1])) << 16);
