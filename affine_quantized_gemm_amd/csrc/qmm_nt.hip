@@ -497,7 +497,9 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
 //
 // Workgroup: 8 wavefronts own a block of 256 columns (16 tiles, 2 per
 // wavefront) and one slice of K (blockIdx.y), walked in chunks of 16 KiB of
-// weights (128 rows at 4 bits, 64 at 8) staged in LDS; the next chunk's
+// weights (128 rows at 4 bits, 64 at 8; 8 KiB where a slice holds at most two
+// 16 KiB chunks, so that its loads and compute still overlap) staged in LDS;
+// the next chunk's
 // weights, activations and scales are loaded into registers while the
 // current one is computed.  A wavefront's tiles are its own for the whole
 // slice, so there is no combine: it stores fp32 partials part[slice][M][N]
@@ -513,32 +515,33 @@ hipError_t launch_nt_b(const MatmulArgs& a) {
 // requests two to one at 128 columns)
 constexpr int NTT_BN = 256;        // columns per workgroup
 constexpr int NTT_THREADS = 512;   // 8 wavefronts, 2 tiles each
-constexpr int NTT_CHUNK_BYTES = 16384;
+constexpr int NTT_CHUNK_BYTES = 16384;  // weights per chunk (the short-slice form: half)
 constexpr int NTT_GMAX = NTT_BN / 32;  // groups a block spans at most
 
-template <int BITS>
+template <int BITS, int CB = NTT_CHUNK_BYTES>
 struct NttFmt {
+    static_assert(CB == NTT_CHUNK_BYTES || CB == NTT_CHUNK_BYTES / 2, "16 or 8 KiB chunks");
     static constexpr int RP = NTT_BN * BITS / 8;              // bytes of a row piece (128 / 256)
-    static constexpr int KC = NTT_CHUNK_BYTES / RP;           // rows per chunk (128 / 64)
+    static constexpr int KC = CB / RP;                        // rows per chunk (128 / 64; 8 KiB: 64 / 32)
     static constexpr int BLK = BITS == 4 ? 64 : 32;           // rows per transpose read (16 / 8 per lane group)
     static constexpr int CPR = RP / 16;                       // 16-byte pieces per row
-    static constexpr int WPT = NTT_CHUNK_BYTES / 16 / NTT_THREADS;  // weight pieces per thread (2)
+    static constexpr int WPT = CB / 16 / NTT_THREADS;         // weight pieces per thread (2; 8 KiB: 1)
     static constexpr int XS = KC + 8;                         // activation row stride in LDS (elements)
     // LDS position of 16-byte piece c of row r (swizzled so that the
     // transpose reads of 16 consecutive rows spread over the banks)
     __device__ static constexpr int swz(int r) { return r & 7; }
 };
 
-template <int DT, int BITS, int RB, bool PART, int SBW>
+template <int DT, int BITS, int RB, bool PART, int SBW, int CB>
 __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ part, int M, int64_t N,
     int64_t K, int gs, int64_t kr) {
-    using F = NttFmt<BITS>;
+    using F = NttFmt<BITS, CB>;
     constexpr int KC = F::KC, XS = F::XS, BLK = F::BLK;
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t* const w_lds = lds;                                                       // [KC][RP], swizzled
-    uint16_t* const x_lds = reinterpret_cast<uint16_t*>(lds + NTT_CHUNK_BYTES);        // [16 RB][XS]
+    uint16_t* const x_lds = reinterpret_cast<uint16_t*>(lds + CB);                     // [16 RB][XS]
     uint16_t* const s_lds = x_lds + 16 * RB * XS;                                      // [GMAX][KC]
     uint16_t* const b_lds = s_lds + NTT_GMAX * KC;                                     // [GMAX][KC]
 
@@ -777,21 +780,22 @@ __global__ __launch_bounds__(NTT_THREADS, 2) void nt_tr_kernel(
             }
 }
 
-template <int BITS, int RB>
+template <int BITS, int RB, int CB>
 constexpr size_t ntt_lds_bytes() {
-    return NTT_CHUNK_BYTES + 2 * (16 * RB * NttFmt<BITS>::XS + 2 * NTT_GMAX * NttFmt<BITS>::KC);
+    return CB + 2 * (16 * RB * NttFmt<BITS, CB>::XS + 2 * NTT_GMAX * NttFmt<BITS, CB>::KC);
 }
 
-template <int DT, int BITS, int RB, bool PART, int SBW>
-hipError_t launch_nt_tr_s(const MatmulArgs& a, int split, int64_t kr) {
-    constexpr size_t lds = ntt_lds_bytes<BITS, RB>();
+template <int DT, int BITS, int RB, bool PART, int SBW, int CB>
+hipError_t launch_nt_tr_c(const MatmulArgs& a, int split, int64_t kr) {
+    constexpr size_t lds = ntt_lds_bytes<BITS, RB, CB>();
     if (lds > 65536) {
         static std::atomic<uint64_t> raised{0};
-        if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&nt_tr_kernel<DT, BITS, RB, PART, SBW>), raised);
+        if (hipError_t e =
+                raise_lds_limit(reinterpret_cast<const void*>(&nt_tr_kernel<DT, BITS, RB, PART, SBW, CB>), raised);
             e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((nt_tr_kernel<DT, BITS, RB, PART, SBW>),
+    hipLaunchKernelGGL((nt_tr_kernel<DT, BITS, RB, PART, SBW, CB>),
                        dim3(static_cast<unsigned>((a.N + NTT_BN - 1) / NTT_BN), static_cast<unsigned>(split)),
                        dim3(NTT_THREADS), lds, a.stream, static_cast<const uint16_t*>(a.x), a.wq,
                        static_cast<const uint16_t*>(a.scales), static_cast<const uint16_t*>(a.biases),
@@ -799,6 +803,18 @@ hipError_t launch_nt_tr_s(const MatmulArgs& a, int split, int64_t kr) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if constexpr (PART) return launch_reduce_partials(DT, a.part, a.y, split, a.M * a.N, a.stream);
     return hipSuccess;
+}
+
+// The chunk size: slices of at most two 16 KiB chunks (K = 4096 on 16
+// slices at 4 bits) go in 8 KiB chunks, so that a chunk's compute overlaps
+// the next chunk's loads; longer slices keep 16 KiB.  Measured at M = 6:
+// 4096 x 4096 (two chunks per slice) 9.9 vs 10.4 us; down 4096 x 14336 and
+// gate/up 14336 x 4096 (eight) 20.1 / 20.0 vs 19.4 / 19.5 us in 8 KiB chunks.
+template <int DT, int BITS, int RB, bool PART, int SBW>
+hipError_t launch_nt_tr_s(const MatmulArgs& a, int split, int64_t kr) {
+    if constexpr (PART)
+        if (kr <= 2 * NttFmt<BITS>::KC) return launch_nt_tr_c<DT, BITS, RB, PART, SBW, NTT_CHUNK_BYTES / 2>(a, split, kr);
+    return launch_nt_tr_c<DT, BITS, RB, PART, SBW, NTT_CHUNK_BYTES>(a, split, kr);
 }
 
 // the scale-run width: every block whole (N a multiple of 256) and 2, 4 or 8
