@@ -23,7 +23,9 @@ LIB_PATH = os.path.join(_PKG, "libqmm.so")
 QMM_F16, QMM_BF16 = 0, 1
 QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_MISALIGNED, QMM_ERR_HIP = 0, -1, -2, -3, -4
 KERNEL_VALU, KERNEL_MFMA_REG, KERNEL_MFMA_PASS, KERNEL_MFMA_TILE16, KERNEL_MFMA_TILE64 = 0, 1, 2, 3, 4
-KERNEL_IDS = (KERNEL_VALU, KERNEL_MFMA_REG, KERNEL_MFMA_PASS, KERNEL_MFMA_TILE16, KERNEL_MFMA_TILE64)
+KERNEL_MFMA_DQLDS = 5
+KERNEL_IDS = (KERNEL_VALU, KERNEL_MFMA_REG, KERNEL_MFMA_PASS, KERNEL_MFMA_TILE16, KERNEL_MFMA_TILE64,
+              KERNEL_MFMA_DQLDS)
 
 _DT = {torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
 

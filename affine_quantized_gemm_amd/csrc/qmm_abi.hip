@@ -282,6 +282,7 @@ const char* qmm_kernel_name(int kernel_id) {
         case QMM_KERNEL_MFMA_PASS: return "mfma_splitfree_pass";
         case QMM_KERNEL_MFMA_TILE16: return "mfma_splitfree_tile16";
         case QMM_KERNEL_MFMA_TILE64: return "mfma_splitfree_tile64";
+        case QMM_KERNEL_MFMA_DQLDS: return "mfma_splitfree_dqlds";
         default: return "?";
     }
 }

@@ -11,6 +11,7 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
         case QMM_KERNEL_MFMA_PASS: return M <= 64;
         case QMM_KERNEL_MFMA_TILE16: return mfma_tile_supports(bits, M, K, TILE_CFG_16);
         case QMM_KERNEL_MFMA_TILE64: return mfma_tile_supports(bits, M, K, TILE_CFG_64);
+        case QMM_KERNEL_MFMA_DQLDS: return mfma_dqlds_supports(bits, M, N, K);
         default: return false;
     }
 }
@@ -117,6 +118,7 @@ hipError_t launch_kernel(int kid, const MatmulArgs& a) {
         case QMM_KERNEL_MFMA_PASS: return launch_mfma_pass(a);
         case QMM_KERNEL_MFMA_TILE16: return launch_mfma_tile(a, TILE_CFG_16);
         case QMM_KERNEL_MFMA_TILE64: return launch_mfma_tile(a, TILE_CFG_64);
+        case QMM_KERNEL_MFMA_DQLDS: return launch_mfma_dqlds(a);
         default: return hipErrorInvalidValue;
     }
 }

@@ -79,6 +79,9 @@ bool mfma_reg_split_supports(int bits, int gs, int64_t M, int64_t N, int64_t K, 
 // to dt (the second kernel of every K split).
 hipError_t launch_reduce_partials(int dt, const float* part, void* y, int split, int64_t mn, hipStream_t st);
 bool mfma_tile_supports(int bits, int64_t M, int64_t K, int cfg);
+// weights dequantized into LDS (64-column tiles, whole K chunks)
+bool mfma_dqlds_supports(int bits, int64_t M, int64_t N, int64_t K);
+hipError_t launch_mfma_dqlds(const MatmulArgs& a);
 // A split count made valid for the tile kernel (every split gets at least
 // one pass); the workspace holds that many partial outputs.
 int tile_split(int bits, int64_t K, int cfg, int split);

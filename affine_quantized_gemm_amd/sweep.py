@@ -155,7 +155,7 @@ def sweep_shape(name, ms, stack_mib, splits=False, shape=None, kernels=None):
 # variant, which the table never selects, is left out.
 FORMAT_MS = (1, 4, 6, 8, 16, 24, 36, 64)
 WIDE_MS = (24, 36, 64)
-MFMA_KERNELS = (1, 2, 3, 4)
+MFMA_KERNELS = (1, 2, 3, 4, 5)
 
 
 def format_shapes():

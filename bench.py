@@ -124,6 +124,7 @@ KERNEL_SOURCES = {
     "mfma_splitfree_pass": ["qmm_mfma_pass.hip", "qmm_mfma_frag.hpp"],
     "mfma_splitfree_tile16": ["qmm_mfma_tile.hpp", "qmm_mfma_frag.hpp"],
     "mfma_splitfree_tile64": ["qmm_mfma_tile.hpp", "qmm_mfma_frag.hpp"],
+    "mfma_splitfree_dqlds": ["qmm_mfma_dqlds.hip", "qmm_mfma_frag.hpp"],
     "nt": ["qmm_nt.hip", "qmm_mfma_frag.hpp"],
 }
 COMMON_SOURCES = ["qmm_device.hpp", "qmm_internal.hpp"]

@@ -74,7 +74,7 @@ def supported(Q, kernel, M, bits=4, gs=64, N=64, K=512, dt=torch.float16):
     return kernel is None or Q.kernel_supported(dt, bits, gs, M, N, K, kernel)
 
 
-KERNELS = [None, 0, 1, 2, 3, 4]
+KERNELS = [None, 0, 1, 2, 3, 4, 5]
 
 
 @pytest.mark.parametrize("dt,bits,gs", COMBOS)
@@ -99,6 +99,32 @@ def test_small_m_all_m(Q, dt, M):
         print(f"small_m {dt} M={M} kernel={kernel}", flush=True)
         ok, worst = run_case(Q, dt, 4, 64, M, N, K, seed=300 + M, kernel=kernel, outlier=0.01)
         assert ok, (kernel, worst)
+
+
+@pytest.mark.parametrize("dt,bits,gs", COMBOS)
+def test_dequant_to_lds_kernel(Q, dt, bits, gs):
+    """The weights-dequantized-into-LDS variant (forced; never selected):
+    every format, 1..4 row blocks with ragged M, several K chunks, against
+    the oracle."""
+    N, K = 192, 512
+    for M in (1, 6, 17, 40, 64):
+        assert Q.kernel_supported(DT[dt], bits, gs, M, N, K, Q.KERNEL_MFMA_DQLDS)
+        print(f"dqlds {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
+        ok, worst = run_case(Q, dt, bits, gs, M, N, K, seed=11 * M + bits + gs, kernel=Q.KERNEL_MFMA_DQLDS,
+                             outlier=0.01)
+        assert ok, (M, worst)
+
+
+def test_dequant_to_lds_kernel_large(Q):
+    """The same variant at the verify shape's width and depth (64 column
+    tiles, 16 chunks of K) and at 4 row blocks."""
+    for dt, bits, gs, M in (("f16", 4, 64, 16), ("bf16", 8, 32, 64)):
+        print(f"dqlds {dt} b{bits} gs{gs} M={M} N=4096 K=4096", flush=True)
+        ok, worst = run_case(Q, dt, bits, gs, M, 4096, 4096, seed=77 + M, kernel=Q.KERNEL_MFMA_DQLDS)
+        assert ok, (dt, bits, worst)
+    assert not Q.kernel_supported(torch.float16, 4, 64, 6, 4096 + 16, 4096, Q.KERNEL_MFMA_DQLDS)  # N % 64
+    assert not Q.kernel_supported(torch.float16, 4, 64, 6, 4096, 4096 + 128, Q.KERNEL_MFMA_DQLDS)  # K % 256
+    assert Q.kernel_supported(torch.float16, 8, 64, 6, 4096, 4096 + 128, Q.KERNEL_MFMA_DQLDS)
 
 
 def kernel_built(Q, kernel, M=6, K=512):
