@@ -41,9 +41,14 @@ bool kernel_supports(int kid, int /*dt*/, int bits, int gs, int64_t M, int64_t N
 //     kernel faster (22.8-23.8 us vs 24.3-25.6 us at M = 64, all four
 //     formats; sweep.py --formats);
 //   * otherwise (6/8-bit with more tiles than resident workgroups), M > 16,
-//     wide N (>= 8192): the 64-column tile kernel: 24.1 / 33.2 us vs
-//     37.6 / 66.6 us (pass) at M = 24 / 64 on the 14336 x 4096 gate/up
-//     projection, 186 / 278 us vs 368 / 669 us on the 151936-column LM head;
+//     wide N (>= 8192): for fp16 the weights dequantized into LDS (packed
+//     fp16 dequantization, one pass per workgroup): 28.1-40.5 us vs
+//     34.9-51.5 us for the 64-column tile kernel at M = 24 / 36 / 64 on
+//     14336 x 4096, every fp16 6/8-bit format (sweep.py --formats); for bf16
+//     (two matrix steps per weight, hi and lo) the 64-column tile kernel:
+//     24.1 / 33.2 us vs 37.6 / 66.6 us (pass) at M = 24 / 64 on the
+//     14336 x 4096 gate/up projection, 186 / 278 us vs 368 / 669 us on the
+//     151936-column LM head;
 //   * M > 32, N from 4096 (at least one 16-column tile per CU): the
 //     16-column tile kernel: 46.0 / 64.7 us vs 56.1 / 65.5 us (pass) at
 //     M = 36 / 64 on the down projection; with fewer tiles than CUs it idles
@@ -63,6 +68,8 @@ int select_kernel(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K) {
         return QMM_KERNEL_MFMA_TILE16;
     if (kernel_supports(QMM_KERNEL_MFMA_REG, dt, bits, gs, M, N, K)) return QMM_KERNEL_MFMA_REG;
     if (M <= 16) return QMM_KERNEL_MFMA_PASS;
+    if (dt == QMM_F16 && bits != 4 && N >= 8192 && kernel_supports(QMM_KERNEL_MFMA_DQLDS, dt, bits, gs, M, N, K))
+        return QMM_KERNEL_MFMA_DQLDS;
     if (kernel_supports(QMM_KERNEL_MFMA_TILE64, dt, bits, gs, M, N, K)) {
         if (N >= 8192) return QMM_KERNEL_MFMA_TILE64;
         if (M > 32 && N >= 4096) return QMM_KERNEL_MFMA_TILE16;

@@ -6,22 +6,27 @@
 // above a handful of rows the matrix-unit kernel (qmm_nax) is the path to
 // beat, and a split-K dispatch of the same product halves its bandwidth.  On
 // Apple GPUs that kernel stages dequantized weight tiles in threadgroup
-// memory; this is that arrangement written for gfx950, kept beside the
-// in-register forms (mfma_splitfree_pass / tile16 / tile64, which build
-// the weight operand in registers) so that the two can be timed against
-// each other on the same shapes.  It is a measured alternative, not a
-// dispatch choice: the selection takes it nowhere (its sweep rows say why).
+// memory; this is that arrangement written for gfx950, beside the in-register
+// forms (mfma_splitfree_reg / pass / tile16 / tile64, which build the weight
+// operand in registers), and both are timed on every format.  The selection
+// takes it for fp16 6/8-bit codes above 16 rows at wide N (8192 columns and
+// more), where it beats the 64-column tile kernel by 5-23 %; elsewhere the
+// in-register forms win (1.4x to 10x): the dequantized tile crosses LDS and
+// each chunk waits on two barriers, and for bf16 every weight costs two
+// matrix steps (hi and lo).
 //
 // Workgroup: 4 wavefronts own a tile of 64 output columns for every row of
-// M (16-row blocks 0..RB-1) and walk K in chunks of KC values (256 at 4 bits,
-// so that a column's chunk is one 128-byte line; 128 at 6 and 8 bits).  Per
+// M (16-row blocks 0..RB-1) and walk K in chunks of 256 values (a column's
+// chunk is one, one and a half or two 128-byte lines at 4, 6, 8 bits).  Per
 // chunk:
-//   * every thread dequantizes whole 32-code runs of one column (4 threads
-//     per column, one or two runs each): w = s q + b in fp32, rounded once to
-//     fp16 (error far inside the accepted bound), or for bf16 split into
+//   * every thread dequantizes two 32-code runs of one column (4 threads per
+//     column): for fp16, two codes at a time, as packed halves -- the codes
+//     become exact fp16 values through the exponent pattern of 1024
+//     (0x6400 | q, minus 1024), then one packed fused multiply-add gives
+//     s q + b rounded once; for bf16, w = s q + b in fp32 split into
 //     hi = RNE(w) and lo = RNE(w - hi) (bf16's 8-bit significand would spend
-//     most of the bound on one rounding), and writes them to the LDS tile
-//     W[column][k];
+//     most of the accepted error on one rounding) -- and writes them to the
+//     LDS tile W[column][k];
 //   * the activation rows of the chunk go to LDS beside it (rows past M stay
 //     zero);
 //   * after one barrier wavefront w reads the B operand of its 16 columns
@@ -29,11 +34,11 @@
 //     A operand of each row block (8 consecutive k of one row) in natural
 //     order, and accumulates v_mfma_f32_16x16x32 steps in fp32 (two per step
 //     for bf16: hi and lo).
-// The next chunk's code words, scales, biases and activations are loaded into
-// registers while the current chunk is computed (after the last chunk, the
-// last one again: the same loads on every path).  Each weight is dequantized
-// once per workgroup; the B operand crosses LDS once (its column owner reads
-// it), the activations once per wavefront.
+// Two chunks are in flight in registers (code words, scales, biases and
+// activations) while one is computed; past the end of K the prefetch reads
+// the last chunk again (the same loads on every path, never staged).  Each
+// weight is dequantized once per workgroup; the B operand crosses LDS once
+// (its column owner reads it), the activations once per wavefront.
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 #include "qmm_mfma_frag.hpp"
@@ -47,12 +52,8 @@ using namespace mf;
 constexpr int DQ_TN = 64;        // columns per workgroup
 constexpr int DQ_THREADS = 256;  // 4 wavefronts, 16 columns each
 
-template <int BITS>
-struct DqFmt {
-    static constexpr int KC = BITS == 4 ? 256 : 128;   // k values per chunk
-    static constexpr int RUNS = KC / 32 / 4;            // 32-code runs per thread (4 threads per column)
-    static constexpr int WS = KC + 8;                   // LDS row stride of W and x (16 bytes of padding)
-};
+constexpr int DQ_KC = 256;        // k values per chunk
+constexpr int DQ_WS = DQ_KC + 8;  // LDS row stride of W and x (16 bytes of padding)
 
 template <int DT, int BITS, int RB>
 __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* __restrict__ x,
@@ -61,10 +62,10 @@ __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* 
                                                              const uint16_t* __restrict__ biases,
                                                              uint16_t* __restrict__ y, int M, int64_t N,
                                                              int64_t K, int gs) {
-    using F = DqFmt<BITS>;
-    constexpr int KC = F::KC, RUNS = F::RUNS, WS = F::WS;
+    constexpr int KC = DQ_KC, WS = DQ_WS;
+    constexpr int RUNS = KC / 32 / 4;                  // 32-code runs per thread (4 threads per column)
     constexpr int NH = DT == DT_BF16 ? 2 : 1;          // bf16: hi and lo tiles
-    constexpr int XP = (16 * RB * KC / 8 + DQ_THREADS - 1) / DQ_THREADS;  // 16-byte activation pieces per thread
+    constexpr int XP = 16 * RB * KC / 8 / DQ_THREADS;  // 16-byte activation pieces per thread
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t* const w_lds = lds;                        // [NH][DQ_TN][WS]
     uint16_t* const x_lds = lds + NH * DQ_TN * WS;      // [16 RB][WS]
@@ -77,24 +78,25 @@ __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* 
     // activation rows M .. 16 RB - 1 stay zero
     for (int i = tid; i < (16 * RB - M) * WS; i += DQ_THREADS) x_lds[M * WS + i] = 0;
 
-    // this thread's dequantization share: column c, runs r = q + 4 j
+    // this thread's dequantization share: column c, runs q and q + 4
     const int c = tid >> 2, q = tid & 3;
     const uint32_t* const wrow = wq + (n0 + c) * row_words;
 
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // (a native vector: stays in registers)
     struct Regs {
         uint32_t w[RUNS][BITS];
-        uint16_t s[RUNS], b[RUNS];
+        uint32_t sb[RUNS];  // scale | bias << 16
         v4u xv[XP];
     };
+    // chunk k0 into r; past the end of K the last chunk again (never staged)
     auto load = [&](int64_t k0, Regs& r) __attribute__((always_inline)) {
+        k0 = k0 < K ? k0 : K - KC;
 #pragma unroll
         for (int j = 0; j < RUNS; ++j) {
             const int64_t kr = k0 + 32 * (q + 4 * j);      // first k of the run
             load_chunk_words<BITS>(wrow + kr * BITS / 32, r.w[j]);
             const int64_t gi = (n0 + c) * G + kr / gs;
-            r.s[j] = scales[gi];
-            r.b[j] = biases[gi];
+            r.sb[j] = static_cast<uint32_t>(scales[gi]) | (static_cast<uint32_t>(biases[gi]) << 16);
         }
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
@@ -107,26 +109,39 @@ __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* 
     auto stage = [&](const Regs& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < RUNS; ++j) {
-            const float s = DtOps<DT>::to_f32(r.s[j]), b = DtOps<DT>::to_f32(r.b[j]);
             const int kl = 32 * (q + 4 * j);
 #pragma unroll
             for (int e = 0; e < 32; e += 8) {
                 uint32_t hi[4], lo[4];
+                if constexpr (DT == DT_F16) {
+                    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+                    const h2_t s2 = __builtin_bit_cast(h2_t, (r.sb[j] & 0xFFFFu) * 0x10001u);
+                    const h2_t b2 = __builtin_bit_cast(h2_t, (r.sb[j] >> 16) * 0x10001u);
+                    const h2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float w0 = __fmaf_rn(s, static_cast<float>(chunk_code<BITS>(r.w[j], e + 2 * t)), b);
-                    const float w1 = __fmaf_rn(s, static_cast<float>(chunk_code<BITS>(r.w[j], e + 2 * t + 1)), b);
-                    const uint16_t h0 = DtOps<DT>::rne(w0), h1 = DtOps<DT>::rne(w1);
-                    hi[t] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-                    if constexpr (NH == 2) {
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t pr = chunk_code<BITS>(r.w[j], e + 2 * t) |
+                                            (chunk_code<BITS>(r.w[j], e + 2 * t + 1) << 16);
+                        const h2_t qv = __builtin_bit_cast(h2_t, pr | 0x64006400u) - k1024;  // exact codes
+                        hi[t] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qv, s2, b2));
+                    }
+                } else {
+                    const float s = DtOps<DT>::to_f32(static_cast<uint16_t>(r.sb[j] & 0xFFFFu));
+                    const float b = DtOps<DT>::to_f32(static_cast<uint16_t>(r.sb[j] >> 16));
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float w0 = __fmaf_rn(s, static_cast<float>(chunk_code<BITS>(r.w[j], e + 2 * t)), b);
+                        const float w1 = __fmaf_rn(s, static_cast<float>(chunk_code<BITS>(r.w[j], e + 2 * t + 1)), b);
+                        const uint16_t h0 = DtOps<DT>::rne(w0), h1 = DtOps<DT>::rne(w1);
                         const uint16_t l0 = DtOps<DT>::rne(w0 - DtOps<DT>::to_f32(h0));
                         const uint16_t l1 = DtOps<DT>::rne(w1 - DtOps<DT>::to_f32(h1));
+                        hi[t] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
                         lo[t] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
                     }
                 }
-                *reinterpret_cast<uint4*>(w_lds + c * WS + kl + e) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                *reinterpret_cast<v4u*>(w_lds + c * WS + kl + e) = v4u{hi[0], hi[1], hi[2], hi[3]};
                 if constexpr (NH == 2)
-                    *reinterpret_cast<uint4*>(w_lds + (DQ_TN + c) * WS + kl + e) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                    *reinterpret_cast<v4u*>(w_lds + (DQ_TN + c) * WS + kl + e) = v4u{lo[0], lo[1], lo[2], lo[3]};
             }
         }
 #pragma unroll
@@ -141,37 +156,45 @@ __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* 
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[b] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int li = lane & 15, lq = lane >> 4;
-    Regs regs;
-    load(0, regs);
-    for (int64_t k0 = 0; k0 < K; k0 += KC) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-        stage(regs);
-        __syncthreads();
-        // the next chunk in flight during this chunk's steps (after the last
-        // chunk the same loads again, never staged: registers loaded on one
-        // path and not on another would be kept in scratch memory)
-        load(k0 + KC < K ? k0 + KC : k0, regs);
+    auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < KC / 32; ++st) {
             const int kk = 32 * st + 8 * lq;
             Frag bh, bl;
             {
-                const uint4 v = *reinterpret_cast<const uint4*>(w_lds + (16 * wave + li) * WS + kk);
+                const v4u v = *reinterpret_cast<const v4u*>(w_lds + (16 * wave + li) * WS + kk);
                 bh.v[0] = v.x; bh.v[1] = v.y; bh.v[2] = v.z; bh.v[3] = v.w;
             }
             if constexpr (NH == 2) {
-                const uint4 v = *reinterpret_cast<const uint4*>(w_lds + (DQ_TN + 16 * wave + li) * WS + kk);
+                const v4u v = *reinterpret_cast<const v4u*>(w_lds + (DQ_TN + 16 * wave + li) * WS + kk);
                 bl.v[0] = v.x; bl.v[1] = v.y; bl.v[2] = v.z; bl.v[3] = v.w;
             }
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 Frag a;
-                const uint4 v = *reinterpret_cast<const uint4*>(x_lds + (16 * b + li) * WS + kk);
+                const v4u v = *reinterpret_cast<const v4u*>(x_lds + (16 * b + li) * WS + kk);
                 a.v[0] = v.x; a.v[1] = v.y; a.v[2] = v.z; a.v[3] = v.w;
                 acc[b] = mfma<DT>(a, bh, acc[b]);
                 if constexpr (NH == 2) acc[b] = mfma<DT>(a, bl, acc[b]);
             }
         }
+    };
+    // chunk i is staged from buffer i % 2, whose next load (chunk i + 2) is
+    // then in flight during the compute of chunks i and i + 1
+    auto step = [&](int64_t k0, Regs& r) __attribute__((always_inline)) {
+        const bool in = k0 < K;
+        if (in) stage(r);
+        __syncthreads();
+        load(k0 + 2 * KC, r);
+        if (in) compute();
+        __syncthreads();  // the chunk's LDS is overwritten next
+    };
+    Regs r0, r1;
+    load(0, r0);
+    load(KC, r1);
+    for (int64_t k0 = 0; k0 < K; k0 += 2 * KC) {
+        step(k0, r0);
+        step(k0 + KC, r1);
     }
     // D[4 lq + r][li] of row block b: output row 16 b + 4 lq + r, column
     // n0 + 16 wave + li
@@ -186,9 +209,8 @@ __global__ __launch_bounds__(DQ_THREADS) void mfma_dqlds_kernel(const uint16_t* 
 
 template <int DT, int BITS, int RB>
 hipError_t launch_dqlds_t(const MatmulArgs& a) {
-    using F = DqFmt<BITS>;
     constexpr int NH = DT == DT_BF16 ? 2 : 1;
-    constexpr size_t lds = static_cast<size_t>(NH * DQ_TN + 16 * RB) * F::WS * sizeof(uint16_t);
+    constexpr size_t lds = static_cast<size_t>(NH * DQ_TN + 16 * RB) * DQ_WS * sizeof(uint16_t);
     if (lds > 65536) {
         static std::atomic<uint64_t> raised{0};
         if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mfma_dqlds_kernel<DT, BITS, RB>), raised);
@@ -216,10 +238,10 @@ hipError_t launch_dqlds_b(const MatmulArgs& a) {
 }  // namespace
 
 bool mfma_dqlds_supports(int bits, int64_t M, int64_t N, int64_t K) {
-    const int64_t kc = bits == 4 ? 256 : 128;
+    (void)bits;
     // (K <= 2^24 keeps every activation and code offset well inside 32-bit
     // products of the index arithmetic)
-    return M >= 1 && M <= 64 && N >= DQ_TN && N % DQ_TN == 0 && K >= kc && K % kc == 0 &&
+    return M >= 1 && M <= 64 && N >= DQ_TN && N % DQ_TN == 0 && K >= DQ_KC && K % DQ_KC == 0 &&
            K <= (int64_t{1} << 24);
 }
 

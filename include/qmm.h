@@ -84,7 +84,7 @@ enum qmm_kernel {
     QMM_KERNEL_MFMA_TILE16 = 3, /* split-free, MFMA, 16-column tiles, activations shared through LDS, M <= 64 */
     QMM_KERNEL_MFMA_TILE64 = 4, /* as TILE16 with 64-column tiles (wide N) */
     QMM_KERNEL_MFMA_DQLDS = 5,  /* split-free, MFMA, weights dequantized into LDS (64-column tiles, M <= 64,
-                                   N a multiple of 64, K of 256 at 4 bits / 128 at 6 and 8); measured, never selected */
+                                   N a multiple of 64, K a multiple of 256) */
     QMM_KERNEL_COUNT = 6
 };
 

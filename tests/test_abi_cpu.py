@@ -165,7 +165,8 @@ def test_dispatch_follows_measured_crossovers():
     wherever it runs (M <= 16 with K <= 4096; above 16 rows on 16-row blocks:
     4-bit when N has more tiles than their slots, any width when 16 rows take
     one tile per workgroup); otherwise M <= 16 -> the
-    pass kernel; M > 16 -> the 64-column tile kernel for wide N, the 16-column
+    pass kernel; M > 16 -> for wide N the weights dequantized into LDS
+    (fp16, 6/8-bit) or the 64-column tile kernel, the 16-column
     tile kernel for M > 32 when N gives every CU a tile, the pass kernel
     otherwise (and wherever the tile kernels cannot run)."""
     import torch
@@ -186,6 +187,11 @@ def test_dispatch_follows_measured_crossovers():
         assert sel(bf16, 6, 128, M, 4096, 4096) == "mfma_splitfree_reg"
         assert sel(f16, 4, 64, M, 1024, 4096) == "mfma_splitfree_reg"
         assert sel(f16, 4, 64, M, 4096, 14336) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
+        # fp16 6/8-bit at wide N: the weights dequantized into LDS (bf16: 64-column tiles)
+        assert sel(f16, 8, 64, M, 14336, 4096) == "mfma_splitfree_dqlds"
+        assert sel(f16, 6, 32, M, 14336, 4096) == "mfma_splitfree_dqlds"
+        assert sel(bf16, 6, 32, M, 14336, 4096) == "mfma_splitfree_tile64"
+        assert sel(f16, 8, 64, M, 14336, 4160) == "mfma_splitfree_tile64"  # K not a multiple of 256
         # 6/8-bit with more tiles than resident workgroups, N >= 4096 but < 8192
         assert sel(f16, 8, 64, M, 6144, 4096) == ("mfma_splitfree_tile16" if M > 32 else "mfma_splitfree_pass")
         # fewer 16-column tiles than CUs, K the register kernel does not take: the pass kernel
@@ -215,7 +221,7 @@ def test_dispatch_matches_the_format_sweep():
             if l.startswith("| shape"):
                 header = [c.strip() for c in l.strip().strip("|").split("|")]
     assert header and len(lines) == 324
-    names = {"reg": 1, "pass": 2, "tile16": 3, "tile64": 4}
+    names = {"reg": 1, "pass": 2, "tile16": 3, "tile64": 4, "dqlds": 5}
     dts = {"f16": torch.float16, "bf16": torch.bfloat16}
     worst = 0.0
     for l in lines:

@@ -103,9 +103,9 @@ def test_small_m_all_m(Q, dt, M):
 
 @pytest.mark.parametrize("dt,bits,gs", COMBOS)
 def test_dequant_to_lds_kernel(Q, dt, bits, gs):
-    """The weights-dequantized-into-LDS variant (forced; never selected):
-    every format, 1..4 row blocks with ragged M, several K chunks, against
-    the oracle."""
+    """The weights-dequantized-into-LDS variant (forced): every format, 1..4
+    row blocks with ragged M, two K chunks (the prefetch past the end reads
+    the last chunk again), against the oracle."""
     N, K = 192, 512
     for M in (1, 6, 17, 40, 64):
         assert Q.kernel_supported(DT[dt], bits, gs, M, N, K, Q.KERNEL_MFMA_DQLDS)
@@ -123,8 +123,8 @@ def test_dequant_to_lds_kernel_large(Q):
         ok, worst = run_case(Q, dt, bits, gs, M, 4096, 4096, seed=77 + M, kernel=Q.KERNEL_MFMA_DQLDS)
         assert ok, (dt, bits, worst)
     assert not Q.kernel_supported(torch.float16, 4, 64, 6, 4096 + 16, 4096, Q.KERNEL_MFMA_DQLDS)  # N % 64
-    assert not Q.kernel_supported(torch.float16, 4, 64, 6, 4096, 4096 + 128, Q.KERNEL_MFMA_DQLDS)  # K % 256
-    assert Q.kernel_supported(torch.float16, 8, 64, 6, 4096, 4096 + 128, Q.KERNEL_MFMA_DQLDS)
+    assert not Q.kernel_supported(torch.float16, 8, 64, 6, 4096, 4096 + 128, Q.KERNEL_MFMA_DQLDS)  # K % 256
+    assert Q.kernel_supported(torch.float16, 6, 64, 6, 4096, 4096 + 256, Q.KERNEL_MFMA_DQLDS)
 
 
 def kernel_built(Q, kernel, M=6, K=512):
