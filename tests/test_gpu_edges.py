@@ -9,7 +9,9 @@ rather than the layout:
   * fp16 activations far from N(0, 1): whole quantization groups of values
     +-100..1000 and single spikes, whose unit sums exceed fp16's range;
   * the narrowest ring form (8-bit, group 32, K = 256, a single activation
-    row of 512 bytes).
+    row of 512 bytes);
+  * 6/8-bit codes at wide N above 16 rows, where fp16 runs the kernel that
+    dequantizes the weights into LDS.
 Every path a caller can reach is run on them: each kernel variant that
 supports the shape (including the register kernel's single-tile, LDS-ring and
 row-block forms), the K split with a workspace, the batched entry point and
@@ -72,7 +74,7 @@ def check_all_paths(Q, P, xs, label, splits=True, batched=True, worst_out=None):
             assert ok, (label, M, what, worst)
 
         for kernel in (None, Q.KERNEL_VALU, Q.KERNEL_MFMA_REG, Q.KERNEL_MFMA_PASS, Q.KERNEL_MFMA_TILE16,
-                       Q.KERNEL_MFMA_TILE64):
+                       Q.KERNEL_MFMA_TILE64, Q.KERNEL_MFMA_DQLDS):
             if kernel is not None and not Q.kernel_supported(tdt, bits, gs, M, N, K, kernel):
                 continue
             what = "dispatch" if kernel is None else Q.kernel_name(kernel)
@@ -192,6 +194,34 @@ def test_large_activations_every_path(Q, dt, bits, gs):
     check_all_paths(Q, P, [large_activations(8, 8192, dt, 13201)], "large-x K=8192", batched=False)
     wk = synth.normal((512, 1024), 0.02, dt, 13300 + bits + gs)
     check_nt(Q, dt, bits, gs, wk, large_activations(6, 512, dt, 13301), "large-x")
+
+
+@pytest.mark.parametrize("kind", ["constant", "tiny", "mixed", "positive", "large-x"])
+@pytest.mark.parametrize("dt,bits,gs", [("f16", 6, 32), ("f16", 8, 128), ("bf16", 8, 64)])
+def test_wide_n_dequant_to_lds_path(Q, kind, dt, bits, gs):
+    """6/8-bit codes at N >= 8192 above 16 rows, where the dispatch takes the
+    kernel that dequantizes the weights into LDS (fp16; bf16 takes the
+    64-column tile kernel): the edge cases above through it and every other
+    path that runs the shape."""
+    N, K = 8192, 512
+    seed = 14000 + 10 * bits + gs
+    if kind in ("constant", "tiny", "mixed"):
+        w = synth.special_groups(kind, N, K, gs, dt, seed)
+    else:
+        w = synth.normal((N, K), 0.02, dt, seed, outlier_frac=0.01)
+        if kind == "positive":
+            w = w.abs()
+    if kind == "large-x" and dt == "f16":
+        xs = [large_activations(M, K, dt, seed + M) for M in (24, 40)]
+    else:
+        xs = [synth.normal((M, K), 1.0, dt, seed + M) for M in (24, 40)]
+        if kind == "positive":
+            xs = [x.abs() for x in xs]
+    P = Prepared(dt, bits, gs, w)
+    want = "mfma_splitfree_dqlds" if dt == "f16" else "mfma_splitfree_tile64"
+    assert Q.kernel_name(Q.select_kernel(DT[dt], bits, gs, 24, N, K)) == want
+    ran = check_all_paths(Q, P, xs, f"{kind} N={N}", batched=False)
+    assert "mfma_splitfree_dqlds" in ran
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
