@@ -35,7 +35,7 @@ EXPORTS = (
     "qmm_probe_stream_read", "qmm_probe_copy",
     "qmm_small_m_ws", "qmm_small_m_workspace_bytes", "qmm_small_m_split_forced", "qmm_split_plan",
     "qmm_small_m_batched", "qmm_small_m_nt", "qmm_small_m_nt_ws", "qmm_small_m_nt_workspace_bytes",
-    "qmm_build_digest", "qmm_small_m_noalloc",
+    "qmm_build_digest", "qmm_small_m_noalloc", "qmm_probe_small_m_loop",
 )
 NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024  # QMM_NOALLOC_SCRATCH_BYTES
 
@@ -86,6 +86,8 @@ def _load():
         "qmm_small_m_nt_workspace_bytes": (i64, [i32, i32, i32, i64, i64, i64]),
         "qmm_build_digest": (ctypes.c_char_p, []),
         "qmm_small_m_noalloc": (i32, [i32, i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "qmm_probe_small_m_loop": (i32, [i32, i32, i32, i64, i64, i64, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), vp, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -116,6 +118,7 @@ qmm_small_m_nt = _lib.qmm_small_m_nt
 qmm_small_m_nt_ws = _lib.qmm_small_m_nt_ws
 qmm_small_m_nt_workspace_bytes = _lib.qmm_small_m_nt_workspace_bytes
 qmm_small_m_noalloc = _lib.qmm_small_m_noalloc
+qmm_probe_small_m_loop = _lib.qmm_probe_small_m_loop
 
 
 def strerror(status: int) -> str:
@@ -262,6 +265,27 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     if dst.numel() * dst.element_size() != nb:
         raise ValueError("src and dst differ in size")
     _check(qmm_probe_copy(src.data_ptr(), dst.data_ptr(), nb, _stream(stream)), "qmm_probe_copy")
+
+
+def probe_small_m_loop(x: torch.Tensor, stack, bits: int, group_size: int, out: torch.Tensor, passes: int = 1,
+                       stream=None):
+    """``passes`` times over ``stack`` (a list of (wq, scales, biases)), one
+    qmm_small_m call per weight set into ``out``, issued from a C loop
+    (measurement helper: the stream-launched rate without Python between
+    the calls)."""
+    if not stack:
+        return
+    for (wq, scales, biases) in stack:
+        _check_small_m(x, wq, scales, biases, bits, group_size, out)
+    n = len(stack)
+    arr = ctypes.c_void_p * n
+    wqs = arr(*[t[0].data_ptr() for t in stack])
+    scs = arr(*[t[1].data_ptr() for t in stack])
+    bis = arr(*[t[2].data_ptr() for t in stack])
+    M, K = x.shape
+    N = stack[0][0].shape[0]
+    _check(qmm_probe_small_m_loop(_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wqs, scs, bis,
+                                  out.data_ptr(), n, passes, _stream(stream)), "qmm_probe_small_m_loop")
 
 
 def _check_small_m(x, wq, scales, biases, bits, group_size, out):

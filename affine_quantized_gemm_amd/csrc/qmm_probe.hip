@@ -120,4 +120,18 @@ int qmm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
+int qmm_probe_small_m_loop(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                           const uint32_t* const* wq, const void* const* scales, const void* const* biases, void* y,
+                           int count, int passes, void* stream) {
+    if (count < 0 || passes < 0) return QMM_ERR_INVALID_ARG;
+    if (count == 0 || passes == 0) return QMM_OK;
+    if (wq == nullptr || scales == nullptr || biases == nullptr) return QMM_ERR_INVALID_ARG;
+    for (int p = 0; p < passes; ++p)
+        for (int i = 0; i < count; ++i)
+            if (const int st = qmm_small_m(dt, bits, group_size, M, N, K, x, wq[i], scales[i], biases[i], y, stream);
+                st != QMM_OK)
+                return st;
+    return QMM_OK;
+}
+
 }  // extern "C"

@@ -352,6 +352,24 @@ def stream_us_per_call(torch, fn, n_calls, reps):
     return e0.elapsed_time(e1) * 1e3 / (reps * n_calls)
 
 
+def c_loop_us_per_call(torch, Q, x, stack, bits, gs, y, passes, reps):
+    """The stack's qmm_small_m calls issued back to back from the library's C
+    loop, stream-launched (no interpreter between launches): the GPU period
+    per call (events) and the host time per launch."""
+    Q.probe_small_m_loop(x, stack, bits, gs, y, passes)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        Q.probe_small_m_loop(x, stack, bits, gs, y, passes)
+    host = time.perf_counter() - t0
+    e1.record()
+    torch.cuda.synchronize()
+    n = reps * passes * len(stack)
+    return e0.elapsed_time(e1) * 1e3 / n, host * 1e6 / n
+
+
 def stream_read_ceiling(torch, Q, B, stack_bytes, reps):
     """A plain coalesced read of B bytes per launch, cycling a pool the size
     of the weight stack, replayed from a HIP graph like the timed step: what
@@ -793,6 +811,11 @@ def main():
         extras["stream_launched_us_per_call"] = {
             f"M{M}": round(stream_us_per_call(torch, lambda M=M: calls(M), S * P, max(2, args.steps // 4)), 3)
             for M in Ms}
+        if args.entry == "small_m" and not args.workspace and args.kernel is None:
+            loop = {M: c_loop_us_per_call(torch, Q, xs[M], stack, bits, gs, ys[M], P, max(2, args.steps // 4))
+                    for M in Ms}
+            extras["c_loop_launched_us_per_call"] = {f"M{M}": round(loop[M][0], 3) for M in Ms}
+            extras["c_loop_host_us_per_launch"] = {f"M{M}": round(loop[M][1], 3) for M in Ms}
         extras["stream_read_ceiling"] = stream_read_ceiling(torch, Q, B, S * B, max(2, args.steps // 2))
     copy_calibration(torch, Q)
 

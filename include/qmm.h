@@ -315,6 +315,20 @@ const char* qmm_kernel_name(int kernel_id);
 int qmm_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, int shape, void* stream);
 int qmm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * qmm_probe_small_m_loop: `passes` times over `count` weight sets, one
+ * qmm_small_m call each (x, y and the formats shared), issued back to back
+ * from this C loop on `stream`: the stream-launched rate of the matmul with
+ * no interpreter between the calls.  `wq`, `scales`, `biases` are HOST
+ * arrays of `count` device pointers (caller-owned, read during the call
+ * only).  Stops at the first call that fails and returns its status;
+ * count < 0, passes < 0 or a NULL pointer array -> QMM_ERR_INVALID_ARG;
+ * count or passes 0 -> QMM_OK with nothing launched.
+ */
+int qmm_probe_small_m_loop(int dt, int bits, int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                           const uint32_t* const* wq, const void* const* scales, const void* const* biases, void* y,
+                           int count, int passes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -159,6 +159,23 @@ def test_probe_validation():
     assert Q.qmm_probe_copy(None, None, 0, None) == Q.QMM_OK
 
 
+def test_probe_small_m_loop_validation():
+    """The C launch loop checks its own arguments, then stops at the first
+    call that qmm_small_m rejects (all before any HIP call)."""
+    arr = ctypes.c_void_p * 2
+    ptrs = arr(A, A)
+    loop = Q.qmm_probe_small_m_loop
+    assert loop(0, 4, 64, 4, 64, 256, A, ptrs, ptrs, ptrs, A, -1, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert loop(0, 4, 64, 4, 64, 256, A, ptrs, ptrs, ptrs, A, 2, -1, None) == Q.QMM_ERR_INVALID_ARG
+    assert loop(0, 4, 64, 4, 64, 256, A, None, ptrs, ptrs, A, 2, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert loop(0, 4, 64, 4, 64, 256, A, ptrs, ptrs, None, A, 2, 1, None) == Q.QMM_ERR_INVALID_ARG
+    assert loop(0, 4, 64, 4, 64, 256, A, None, None, None, A, 0, 1, None) == Q.QMM_OK
+    assert loop(0, 4, 64, 4, 64, 256, A, ptrs, ptrs, ptrs, A, 2, 0, None) == Q.QMM_OK
+    # each call's own validation: a bad format, a misaligned first weight set
+    assert loop(0, 5, 64, 4, 64, 256, A, ptrs, ptrs, ptrs, A, 2, 1, None) == Q.QMM_ERR_UNSUPPORTED
+    assert loop(0, 4, 64, 4, 64, 256, A, arr(MIS, A), ptrs, ptrs, A, 2, 1, None) == Q.QMM_ERR_MISALIGNED
+
+
 def test_dispatch_follows_measured_crossovers():
     """qmm_select_kernel encodes the crossovers measured on MI355X
     (affine_quantized_gemm_amd/sweep.py): the register-resident MFMA kernel

@@ -1,6 +1,6 @@
 """The measurement helpers do what qmm.h says: the copy moves every byte,
 the streaming read runs to completion on sizes with and without a ragged
-tail of 16-byte units."""
+tail of 16-byte units, and the C launch loop makes the calls it names."""
 
 import pytest
 import torch
@@ -35,3 +35,20 @@ def test_stream_read_runs(Q, nbytes, grid, shape):
     torch.cuda.synchronize()
     # all-ones data XOR-reduces to a value that is never the kernel's trigger
     assert int(sink.abs().sum()) == 0
+
+
+def test_small_m_loop_matches_calls(Q):
+    """The C launch loop makes the same calls as qmm_small_m one by one:
+    after it, y holds the product with the last weight set, bit for bit."""
+    import synth
+    M, N, K, bits, gs = 6, 1024, 2048, 4, 64
+    stack = []
+    for i in range(3):
+        w = synth.normal((N, K), 0.02, "f16", 18000 + i).cuda()
+        stack.append(Q.quantize(w, bits, gs))
+    x = synth.normal((M, K), 1.0, "f16", 18100).cuda()
+    y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    Q.probe_small_m_loop(x, stack, bits, gs, y, passes=2)
+    ref = Q.small_m(x, *stack[-1], bits, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
