@@ -492,8 +492,15 @@ def measure_cell(torch, Q, synth, cell, steps, warmup, stack_mib, ceilings):
     us, kern = [], []
     for M in Ms:
         g = capture(torch, lambda M=M: calls(M))
-        for _ in range(warmup):
+        # at least `warmup` replays and 30 ms of them: a cell follows a run of
+        # cells with microsecond kernels, and a first timed block right after
+        # a short warm-up read up to 6 % slow on the long LM-head calls
+        t_w = time.perf_counter()
+        n_w = 0
+        while n_w < warmup or time.perf_counter() - t_w < 0.03:
             g.replay()
+            torch.cuda.synchronize()
+            n_w += 1
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
