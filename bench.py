@@ -71,6 +71,7 @@ def alg_bytes(M, N, K, bits, gs):
 WORKLOADS = {
     # name: (dtype, bits, gs, M list, N, K)
     "verify": ("f16", 4, 64, (4, 6), 4096, 4096),
+    "kv": ("f16", 4, 64, (4, 6), 1024, 4096),
     "tiny": ("f16", 4, 64, (4,), 512, 512),
     "decode_down": ("f16", 4, 64, (8, 16, 32, 36, 48, 64), 4096, 14336),
     "decode_gateup": ("f16", 4, 64, (8, 16, 32, 36, 48, 64), 14336, 4096),
