@@ -267,14 +267,13 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     _check(qmm_probe_copy(src.data_ptr(), dst.data_ptr(), nb, _stream(stream)), "qmm_probe_copy")
 
 
-def probe_small_m_loop(x: torch.Tensor, stack, bits: int, group_size: int, out: torch.Tensor, passes: int = 1,
-                       stream=None):
-    """``passes`` times over ``stack`` (a list of (wq, scales, biases)), one
-    qmm_small_m call per weight set into ``out``, issued from a C loop
-    (measurement helper: the stream-launched rate without Python between
-    the calls)."""
+def small_m_loop_args(x: torch.Tensor, stack, bits: int, group_size: int, out: torch.Tensor) -> tuple:
+    """Validated leading arguments of qmm_probe_small_m_loop for ``stack`` (a
+    non-empty list of (wq, scales, biases)) with x and ``out``: the C call
+    then takes ``(*args, passes, stream)``.  The tensors must stay alive
+    while the tuple is used."""
     if not stack:
-        return
+        raise ValueError("empty stack")
     for (wq, scales, biases) in stack:
         _check_small_m(x, wq, scales, biases, bits, group_size, out)
     n = len(stack)
@@ -284,8 +283,19 @@ def probe_small_m_loop(x: torch.Tensor, stack, bits: int, group_size: int, out: 
     bis = arr(*[t[2].data_ptr() for t in stack])
     M, K = x.shape
     N = stack[0][0].shape[0]
-    _check(qmm_probe_small_m_loop(_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wqs, scs, bis,
-                                  out.data_ptr(), n, passes, _stream(stream)), "qmm_probe_small_m_loop")
+    return (_dt(x.dtype), bits, group_size, M, N, K, x.data_ptr(), wqs, scs, bis, out.data_ptr(), n)
+
+
+def probe_small_m_loop(x: torch.Tensor, stack, bits: int, group_size: int, out: torch.Tensor, passes: int = 1,
+                       stream=None):
+    """``passes`` times over ``stack`` (a list of (wq, scales, biases)), one
+    qmm_small_m call per weight set into ``out``, issued from a C loop
+    (measurement helper: the stream-launched rate without Python between
+    the calls; ``small_m_loop_args`` validates once for repeated calls)."""
+    if not stack:
+        return
+    _check(qmm_probe_small_m_loop(*small_m_loop_args(x, stack, bits, group_size, out), passes, _stream(stream)),
+           "qmm_probe_small_m_loop")
 
 
 def _check_small_m(x, wq, scales, biases, bits, group_size, out):

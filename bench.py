@@ -356,17 +356,24 @@ def stream_us_per_call(torch, fn, n_calls, reps):
 def c_loop_us_per_call(torch, Q, x, stack, bits, gs, y, passes, reps):
     """The stack's qmm_small_m calls issued back to back from the library's C
     loop, stream-launched (no interpreter between launches): the GPU period
-    per call (events) and the host time per launch."""
-    Q.probe_small_m_loop(x, stack, bits, gs, y, passes)
+    per call (events) and the host time per launch.  The arguments are
+    validated once, before the timed calls."""
+    args = Q.small_m_loop_args(x, stack, bits, gs, y)
+    sh = torch.cuda.current_stream().cuda_stream
+    if Q.qmm_probe_small_m_loop(*args, passes, sh) != Q.QMM_OK:
+        raise SystemExit("qmm_probe_small_m_loop failed")
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = 0
     e0.record()
     t0 = time.perf_counter()
     for _ in range(reps):
-        Q.probe_small_m_loop(x, stack, bits, gs, y, passes)
+        st |= Q.qmm_probe_small_m_loop(*args, passes, sh)
     host = time.perf_counter() - t0
     e1.record()
     torch.cuda.synchronize()
+    if st != Q.QMM_OK:
+        raise SystemExit("qmm_probe_small_m_loop failed")
     n = reps * passes * len(stack)
     return e0.elapsed_time(e1) * 1e3 / n, host * 1e6 / n
 
