@@ -497,7 +497,7 @@ def measure_cell(torch, Q, synth, cell, steps, warmup, stack_mib, ceilings):
                 else:
                     Q.small_m(xs[M], wq, sc, bi, bits, gs, out=ys[M])
 
-    us, kern = [], []
+    us, kern, cl = [], [], []
     for M in Ms:
         g = capture(torch, lambda M=M: calls(M))
         # at least `warmup` replays and 30 ms of them: a cell follows a run of
@@ -518,6 +518,8 @@ def measure_cell(torch, Q, synth, cell, steps, warmup, stack_mib, ceilings):
         torch.cuda.synchronize()
         us.append(e0.elapsed_time(e1) * 1e3 / (steps * S * P))
         del g
+        if entry != "ws":  # the same calls stream-launched from the library's C loop
+            cl.append(c_loop_us_per_call(torch, Q, xs[M], mats, bits, gs, ys[M], P, steps)[0])
         if entry == "ws":
             k, sp = Q.split_plan(tdt, bits, gs, M, N, K)
             kern.append(KSHORT[Q.kernel_name(k)] + (f"/split{sp}" if sp > 1 else ""))
@@ -531,6 +533,8 @@ def measure_cell(torch, Q, synth, cell, steps, warmup, stack_mib, ceilings):
            "gbs": [round(B / (u * 1e-6) / 1e9, 1) for u in us],
            "frac": [round(alg_bytes(M, N, K, bits, gs) / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for M, u in zip(Ms, us)],
            "kernel": kern, "stack": S}
+    if cl:
+        rec["c_loop_us"] = [round(u, 3) for u in cl]
     if ceil is not None:
         rec["ceil_us"] = ceil
         rec["of_ceil"] = [round(ceil / u, 3) for u in us]
