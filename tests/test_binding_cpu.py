@@ -120,3 +120,17 @@ def test_quantize_and_dequantize_check_shapes():
     consistent(lambda: Q.dequantize(wq, sc, bi, 4, 64))
     rejected(lambda: Q.dequantize(wq, sc, bi, 6, 64), "wq has shape")
     rejected(lambda: Q.dequantize(wq, sc, bi[:8], 4, 64), "biases has shape")
+
+
+def test_small_m_loop_args_checks_every_weight_set():
+    """The C launch loop's argument builder validates the weight sets of the
+    stack against x and out (on host tensors a consistent set stops at the
+    device check), and refuses an empty stack."""
+    x, wq, sc, bi = operands()
+    out = torch.zeros((4, 48), dtype=F16)
+    with pytest.raises(ValueError, match="empty stack"):
+        Q.small_m_loop_args(x, [], 4, 64, out)
+    consistent(lambda: Q.small_m_loop_args(x, [(wq, sc, bi), (wq, sc, bi)], 4, 64, out))
+    _, wq_b, sc_b, bi_b = operands(N=64)  # a second weight set of another width
+    rejected(lambda: Q.small_m_loop_args(x, [(wq_b, sc_b, bi_b), (wq, sc, bi)], 4, 64, out), "out has shape")
+    rejected(lambda: Q.small_m_loop_args(x, [(wq, sc_b, bi)], 4, 64, out), "scales has shape")
