@@ -89,6 +89,32 @@ __host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
     return x > 2048 ? x : 2048;
 }
 
+// Whole-line weight loads (single-tile 4-bit vector form).  In the matrix-core
+// layout a lane's 16 bytes of a k-block sit in the row of its tile column, so
+// a wavefront's fragment loads touch 16 rows x 64 bytes -- half lines -- per
+// instruction.  Here the wavefront loads its K range of the tile's 16 rows as
+// whole 128-byte lines instead (consecutive lanes, consecutive 16-byte
+// pieces of a row), writes them to its own LDS region (over its staged
+// activations, which it has read back by then; rows padded by 16 bytes) and
+// reads its fragments from there: no barrier, the region is the
+// wavefront's own.  Measured against the fragment loads on one box (graph-
+// replayed, alternated): verify 4096^2 at M = 1 / 4 / 6 / 8 4.78 / 4.85-4.91
+// / 4.93 / 5.04 vs 5.06-5.10 / 5.12-5.14 / 5.14-5.16 / 5.20-5.23 us, but
+// 12- and 16-row blocks 0.06-0.2 us slower (their activation staging keeps
+// the LDS busy), so the host launches it for one block of at most 8 rows.
+template <int BITS, bool MULTI, bool VEC>
+__host__ __device__ constexpr bool reg_wl() {
+    return !MULTI && VEC && BITS == 4;
+}
+// bytes of one staged row: the wavefront's k-blocks at 4 bits, plus padding
+__host__ __device__ constexpr int wl_row_bytes(int kpw, int kblk) { return kpw * kblk / 2 + 16; }
+template <int BITS, bool MULTI, bool VEC>
+__host__ __device__ inline int reg_wave_lds(int M, int kpw, int kblk) {
+    const int x = wave_lds_bytes(M, kpw, kblk);
+    const int w = reg_wl<BITS, MULTI, VEC>() ? 16 * wl_row_bytes(kpw, kblk) : 0;
+    return x > w ? x : w;
+}
+
 // Cooperative form of the scales and biases (multi-tile workgroups of the
 // vector form): the 16 rows x G values of a tile are one contiguous block per
 // array; the workgroup fetches it with one 16-byte chunk per lane (a few
@@ -214,7 +240,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // and the partials are combined in the same order, so the results are
 // bit-identical to that form (and to its multi-tile, batched and row-block
 // relatives) with fewer, longer wavefronts.
-template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS, int V = 1>
+template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT, bool ROWS, int V = 1,
+          bool WLT = false>
 __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int64_t N, int64_t K, int64_t ldk,
@@ -237,7 +264,12 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     constexpr int PL = DMA && MH ? 32 : 64;
     static_assert(!DMA || COOP, "the weight ring carries the cooperative scale/bias blocks");
     // (row blocks: sized for a whole block, the same in every workgroup)
-    const int wave_lds = DMA ? dma_wave_lds(MH) : wave_lds_bytes(ROWS ? 16 : M, KPW, F::KBLK);
+    const int wave_lds = DMA ? dma_wave_lds(MH) : reg_wave_lds<BITS, MULTI, VEC>(ROWS ? 16 : M, KPW, F::KBLK);
+    // (the whole-line form is its own instantiation, launched where it pays:
+    // one block of at most 8 rows; with more rows the activation staging
+    // keeps the LDS busy and the fragment loads are faster.  The LDS is
+    // sized for it in either instantiation.)
+    constexpr bool WL = reg_wl<BITS, MULTI, VEC>() && WLT && !ROWS;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -288,6 +320,17 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const uint32_t w_off = lane_row * static_cast<uint32_t>(row_bytes) +
                            static_cast<uint32_t>((kb0 * F::KBLK + jj * F::SEG) * BITS / 8);
     const uint32_t s_off = lane_row * static_cast<uint32_t>(G) + static_cast<uint32_t>(kb0 * F::KBLK / GS);
+    // whole-line form: load j, lane l takes 16-byte piece (64 j + l) of the
+    // wavefront's range, row-major over the tile's 16 rows (PPR pieces a row)
+    constexpr int PPR = KPW * F::KBLK / 32;
+    uint32_t wl_off[KPW];
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+        const int pc = 64 * j + lane;
+        const int64_t row = narrow ? min(static_cast<int64_t>(pc / PPR), N - 1) : static_cast<int64_t>(pc / PPR);
+        wl_off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(row_bytes) +
+                    static_cast<uint32_t>(kb0 * F::KBLK / 2 + (pc % PPR) * 16);
+    }
     auto tile_col0 = [&](int64_t tile) -> int64_t {
         const int64_t c0 = tile * 16;
         return (narrow || c0 + 16 <= N) ? c0 : N - 16;
@@ -398,7 +441,9 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
         const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wq) + col0 * row_bytes;
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
-            if constexpr (VEC) {
+            if constexpr (WL) {
+                load_segment<BITS, F::SEG_WORDS, !ROWS>(reinterpret_cast<const uint32_t*>(wbase + wl_off[i]), r.w[i]);
+            } else if constexpr (VEC) {
                 // VEC: the k-blocks cover K exactly
                 load_segment<BITS, F::SEG_WORDS, !ROWS>(
                     reinterpret_cast<const uint32_t*>(wbase + w_off + i * (F::KBLK * BITS / 8)), r.w[i]);
@@ -649,6 +694,23 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             if constexpr (coop && !DMA) {
                 // this wavefront's scales and biases of tile t, from the block in LDS
                 r.sb.from_lds(sblk + (parity * 2 * 16 + c) * sb_row + (kb0 * F::KBLK / GS) * 2, 16 * sb_row);
+            }
+            if constexpr (WL) {
+                // whole lines -> this wavefront's LDS region -> fragment order
+                // (lane (c, jj) of k-block i: row c, bytes 64 i + 16 jj)
+                constexpr int WRS = wl_row_bytes(KPW, F::KBLK);
+                uint8_t* ws = lds + wave * wave_lds;
+    #pragma unroll
+                for (int j = 0; j < KPW; ++j) {
+                    const int pc = 64 * j + lane;
+                    *reinterpret_cast<uint4*>(ws + (pc / PPR) * WRS + (pc % PPR) * 16) =
+                        make_uint4(r.w[j][0], r.w[j][1], r.w[j][2], r.w[j][3]);
+                }
+    #pragma unroll
+                for (int i = 0; i < KPW; ++i) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(ws + c * WRS + i * (F::KBLK / 2) + jj * 16);
+                    r.w[i][0] = v.x; r.w[i][1] = v.y; r.w[i][2] = v.z; r.w[i][3] = v.w;
+                }
             }
             float4_t yacc[V];
     #pragma unroll
@@ -918,7 +980,8 @@ template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool M
 size_t reg_lds_bytes(int64_t M, int64_t K) {
     constexpr bool dma = reg_dma<DT, BITS, GS, KPW, VEC, MULTI, MH>();
     constexpr size_t DMA_SLOTS = static_cast<size_t>(dma_slots<BITS>());
-    const size_t wave_lds = dma ? dma_wave_lds(MH) : wave_lds_bytes(static_cast<int>(M), KPW, Fmt<DT, BITS, GS>::KBLK);
+    const size_t wave_lds =
+        dma ? dma_wave_lds(MH) : reg_wave_lds<BITS, MULTI, VEC>(static_cast<int>(M), KPW, Fmt<DT, BITS, GS>::KBLK);
     return static_cast<size_t>(W) * wave_lds +
            (dma ? (DMA_SLOTS + 1) * static_cast<size_t>(dma_sb_block_bytes(K / GS))
             : MULTI && reg_coop<DT, BITS, GS, KPW, VEC>() ? static_cast<size_t>(sb_lds_bytes(K / GS))
@@ -929,7 +992,7 @@ size_t reg_lds_bytes(int64_t M, int64_t K) {
 // Launch over K range kr of rows a.K long: kr = a.K unsplit, a.K / S split
 // S ways (grid.y = S, each slice with its share of the resident workgroups).
 template <int DT, int BITS, int GS, int W, int KPW, bool VEC, bool MULTI, bool MH, bool SPLIT = false,
-          bool ROWS = false, int V = 1>
+          bool ROWS = false, int V = 1, bool WLT = false>
 hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
     const int S = SPLIT ? a.split : 1;
     const int RB = ROWS ? static_cast<int>((a.M + 15) / 16) : 1;
@@ -970,12 +1033,12 @@ hipError_t launch_shape_m(const MatmulArgs& a, int64_t kr) {
         // above the default dynamic-LDS limit: raise it once per kernel and device
         static std::atomic<uint64_t> raised{0};
         if (hipError_t e = raise_lds_limit(
-                reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V>),
+                reinterpret_cast<const void*>(&mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V, WLT>),
                 raised);
             e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V>),
+    hipLaunchKernelGGL((mfma_reg_kernel<DT, BITS, GS, W, KPW, VEC, MULTI, MH, SPLIT, ROWS, V, WLT>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(SPLIT ? S : nb),
                             static_cast<unsigned>(RB)),
                        dim3(64 * W), lds, a.stream,
@@ -1002,6 +1065,8 @@ hipError_t launch_shape(const MatmulArgs& a) {
                 return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, true>(a, a.K);
         return launch_shape_m<DT, BITS, GS, W, KPW, VEC, true, false>(a, a.K);
     }
+    if constexpr (reg_wl<BITS, false, VEC>())
+        if (a.M <= 8) return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false, false, false, false, 1, true>(a, a.K);
     return launch_shape_m<DT, BITS, GS, W, KPW, VEC, false, false>(a, a.K);
 }
 
@@ -1026,6 +1091,12 @@ inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, i
 // sub-slice, lose at 6 rows and keep 16 wavefronts.
 template <int DT, int BITS, int GS, bool ROWS>
 hipError_t launch_single_halved(const MatmulArgs& a, int kpw) {
+    // (4-bit, one block of at most 8 rows: the whole-line instantiation)
+    if constexpr (BITS == 4 && !ROWS)
+        if (a.M <= 8) {
+            if (kpw == 1) return launch_shape_m<DT, BITS, GS, 8, 2, true, false, false, false, false, 2, true>(a, a.K);
+            if (kpw == 2) return launch_shape_m<DT, BITS, GS, 8, 4, true, false, false, false, false, 2, true>(a, a.K);
+        }
     if (kpw == 1) return launch_shape_m<DT, BITS, GS, 8, 2, true, false, false, false, ROWS, 2>(a, a.K);
     if (kpw == 2) return launch_shape_m<DT, BITS, GS, 8, 4, true, false, false, false, ROWS, 2>(a, a.K);
     if constexpr (BITS != 4)
