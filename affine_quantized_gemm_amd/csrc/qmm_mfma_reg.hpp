@@ -102,16 +102,17 @@ __host__ __device__ inline int wave_lds_bytes(int M, int kpw, int kblk) {
 // / 4.93 / 5.04 vs 5.06-5.10 / 5.12-5.14 / 5.14-5.16 / 5.20-5.23 us, but
 // 12- and 16-row blocks 0.06-0.2 us slower (their activation staging keeps
 // the LDS busy), so the host launches it for one block of at most 8 rows.
+// (4- and 8-bit codes: a k-block is 64 bytes of a row, a lane's quarter 16.)
 template <int BITS, bool MULTI, bool VEC>
 __host__ __device__ constexpr bool reg_wl() {
-    return !MULTI && VEC && BITS == 4;
+    return !MULTI && VEC && (BITS == 4 || BITS == 8);
 }
-// bytes of one staged row: the wavefront's k-blocks at 4 bits, plus padding
-__host__ __device__ constexpr int wl_row_bytes(int kpw, int kblk) { return kpw * kblk / 2 + 16; }
+// bytes of one staged row: the wavefront's k-blocks, plus padding
+__host__ __device__ constexpr int wl_row_bytes(int kpw, int kblk_bytes) { return kpw * kblk_bytes + 16; }
 template <int BITS, bool MULTI, bool VEC>
 __host__ __device__ inline int reg_wave_lds(int M, int kpw, int kblk) {
     const int x = wave_lds_bytes(M, kpw, kblk);
-    const int w = reg_wl<BITS, MULTI, VEC>() ? 16 * wl_row_bytes(kpw, kblk) : 0;
+    const int w = reg_wl<BITS, MULTI, VEC>() ? 16 * wl_row_bytes(kpw, kblk * BITS / 8) : 0;
     return x > w ? x : w;
 }
 
@@ -270,6 +271,8 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     // keeps the LDS busy and the fragment loads are faster.  The LDS is
     // sized for it in either instantiation.)
     constexpr bool WL = reg_wl<BITS, MULTI, VEC>() && WLT && !ROWS;
+    static_assert(!WL || (F::SEG_WORDS == 4 && F::SEG * BITS / 8 == 16 && F::KBLK * BITS / 8 == 64),
+                  "whole-line staging: 64-byte k-blocks of four 16-byte quarters");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -322,14 +325,14 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
     const uint32_t s_off = lane_row * static_cast<uint32_t>(G) + static_cast<uint32_t>(kb0 * F::KBLK / GS);
     // whole-line form: load j, lane l takes 16-byte piece (64 j + l) of the
     // wavefront's range, row-major over the tile's 16 rows (PPR pieces a row)
-    constexpr int PPR = KPW * F::KBLK / 32;
+    constexpr int PPR = KPW * F::KBLK * BITS / 128;
     uint32_t wl_off[KPW];
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
         const int pc = 64 * j + lane;
         const int64_t row = narrow ? min(static_cast<int64_t>(pc / PPR), N - 1) : static_cast<int64_t>(pc / PPR);
         wl_off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(row_bytes) +
-                    static_cast<uint32_t>(kb0 * F::KBLK / 2 + (pc % PPR) * 16);
+                    static_cast<uint32_t>(kb0 * F::KBLK * BITS / 8 + (pc % PPR) * 16);
     }
     auto tile_col0 = [&](int64_t tile) -> int64_t {
         const int64_t c0 = tile * 16;
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
             if constexpr (WL) {
                 // whole lines -> this wavefront's LDS region -> fragment order
                 // (lane (c, jj) of k-block i: row c, bytes 64 i + 16 jj)
-                constexpr int WRS = wl_row_bytes(KPW, F::KBLK);
+                constexpr int WRS = wl_row_bytes(KPW, F::KBLK * BITS / 8);
                 uint8_t* ws = lds + wave * wave_lds;
     #pragma unroll
                 for (int j = 0; j < KPW; ++j) {
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(64 * W, (64 * W >= 1024 ? 4 : 2)) void mfma_reg_ker
                 }
     #pragma unroll
                 for (int i = 0; i < KPW; ++i) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(ws + c * WRS + i * (F::KBLK / 2) + jj * 16);
+                    const uint4 v = *reinterpret_cast<const uint4*>(ws + c * WRS + i * (F::KBLK * BITS / 8) + jj * 16);
                     r.w[i][0] = v.x; r.w[i][1] = v.y; r.w[i][2] = v.z; r.w[i][3] = v.w;
                 }
             }
@@ -1091,11 +1094,13 @@ inline bool reg_split_shape(int bits, int gs, int64_t M, int64_t N, int64_t K, i
 // sub-slice, lose at 6 rows and keep 16 wavefronts.
 template <int DT, int BITS, int GS, bool ROWS>
 hipError_t launch_single_halved(const MatmulArgs& a, int kpw) {
-    // (4-bit, one block of at most 8 rows: the whole-line instantiation)
-    if constexpr (BITS == 4 && !ROWS)
+    // (4/8-bit, one block of at most 8 rows: the whole-line instantiation)
+    if constexpr (reg_wl<BITS, false, true>() && !ROWS)
         if (a.M <= 8) {
             if (kpw == 1) return launch_shape_m<DT, BITS, GS, 8, 2, true, false, false, false, false, 2, true>(a, a.K);
             if (kpw == 2) return launch_shape_m<DT, BITS, GS, 8, 4, true, false, false, false, false, 2, true>(a, a.K);
+            if constexpr (BITS != 4)
+                if (kpw == 4) return launch_shape_m<DT, BITS, GS, 8, 8, true, false, false, false, false, 2, true>(a, a.K);
         }
     if (kpw == 1) return launch_shape_m<DT, BITS, GS, 8, 2, true, false, false, false, ROWS, 2>(a, a.K);
     if (kpw == 2) return launch_shape_m<DT, BITS, GS, 8, 4, true, false, false, false, ROWS, 2>(a, a.K);
