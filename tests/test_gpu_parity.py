@@ -407,6 +407,37 @@ def test_batched(Q, dt, bits, gs, B, M, N, K):
         assert torch.equal(y[b].view(torch.int16), yb.view(torch.int16)), b
 
 
+@pytest.mark.parametrize("dt,bits,gs,K", [("f16", 4, 64, 512), ("bf16", 4, 32, 2048), ("f16", 4, 128, 4096),
+                                          ("bf16", 8, 64, 1024), ("f16", 8, 128, 4096), ("bf16", 8, 32, 512)])
+def test_whole_line_weight_loads(Q, dt, bits, gs, K):
+    """The register kernel's whole-line instantiation (4/8-bit, one block of
+    at most 8 rows) and the fragment-load one just above it (9, 12 rows), on
+    narrow N (rows clamped to N - 1), one exact tile, a ragged last tile and
+    several tiles; every output against the oracle, and a batched call
+    bit-identical to the standalone one."""
+    for N in (5, 16, 37, 1027):
+        w = synth.normal((N, K), 0.02, dt, 19000 + N + bits + gs)
+        owq, osc, obi = oracle_quant(w, dt, bits, gs)
+        wq, sc, bi = synth.from_oracle(owq).cuda(), synth.from_oracle(osc, dt).cuda(), synth.from_oracle(obi, dt).cuda()
+        for M in (1, 5, 8, 9, 12):
+            print(f"whole-line {dt} b{bits} gs{gs} M={M} N={N} K={K}", flush=True)
+            x = synth.normal((M, K), 1.0, dt, 19100 + M)
+            y = Q.small_m(x.cuda(), wq, sc, bi, bits, gs)
+            torch.cuda.synchronize()
+            yo, T = O.qmm(synth.to_oracle(x), owq, osc, obi, dt, bits, gs)
+            ok, worst = O.within_tolerance(O.to_f64(synth.to_oracle(y), dt), yo, T)
+            assert ok, (N, M, worst)
+    B, M, N = 3, 6, 40  # (a ragged last tile; entry sizes multiples of 16 bytes, as batching requires)
+    xs = synth.normal((B, M, K), 1.0, dt, 19200).cuda()
+    ents = [Q.quantize(synth.normal((N, K), 0.02, dt, 19300 + b).cuda(), bits, gs) for b in range(B)]
+    wq, sc, bi = (torch.stack([e[i] for e in ents]) for i in range(3))
+    yb = Q.small_m_batched(xs, wq, sc, bi, bits, gs)
+    for b in range(B):
+        y1 = Q.small_m(xs[b], wq[b], sc[b], bi[b], bits, gs)
+        torch.cuda.synchronize()
+        assert torch.equal(yb[b].view(torch.int16), y1.view(torch.int16)), b
+
+
 def nt_case(Q, dt, bits, gs, M, N, K, seed, outlier=0.0):
     """qmm_small_m_nt on W [K, N] quantized along N, against the oracle."""
     w = synth.normal((K, N), 0.02, dt, seed, outlier_frac=outlier)
